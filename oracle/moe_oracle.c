@@ -1,0 +1,448 @@
+/*
+ * moe_oracle.c -- plain, slow CPU reference for the MoE dispatch-permute ->
+ * grouped SwiGLU MLP -> combine-unpermute path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library; floating point is evaluated
+ * in double precision except where a float decides an integer (fp8 scale and
+ * code selection), which is taken in float as the GPU kernels take it.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P1] Megatron-LM PR #6800 "Reuse caller-owned HybridEP dispatch and expert
+ *        output buffers"
+ *   [P2] DeepEP PR #716 "perf: reuse HybridEP routing allgather buffer"
+ *   [P3] NeMo-Automodel PR #3931 "perf(moe): sync-free HybridEP dispatch
+ *        (capacity mode, equal token counts)"
+ *   [P4] Megatron-LM PR #4632 "moe: add DeepEP V2 ElasticBuffer support to MoE
+ *        flex dispatcher"
+ *   [P5] TensorRT-LLM PR #16190 "Update CuTeDSL MegaMoE kernels"
+ *
+ * The pages state the interface of the operation, not its arithmetic, so each
+ * function below is the plain definition of what that interface returns.
+ * Where the pages leave a choice open the reading taken is written next to
+ * the code that applies it.
+ *
+ * Pins: every function here is checked by the CPU tests against something
+ * other than itself (brute force, invariants, numpy/torch library routines,
+ * page-printed values).  No function is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_FLAG_CAPACITY   1  /* some expert received more copies than its capacity   */
+#define ORC_FLAG_OUT_ROWS   2  /* padded segments need more rows than the output holds */
+#define ORC_FLAG_BAD_EXPERT 4  /* a dense entry outside [-1, E)                        */
+#define ORC_FLAG_DUPLICATE  8  /* repeated expert in a dense row / too many in a sparse row */
+
+enum { ORC_DENSE_I16 = 0, ORC_DENSE_I32 = 1, ORC_SPARSE_U8 = 2 };
+
+/* ------------------------------------------------------------------------ */
+/* threads                                                                   */
+/* ------------------------------------------------------------------------ */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* number formats, from their definitions                                     */
+/* ------------------------------------------------------------------------ */
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits.  Round a double
+ * to the nearest bfloat16 value, ties to even, overflow to infinity. */
+uint16_t orc_bf16_from_double(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int ex;
+    frexp(a, &ex);                    /* a in [2^(ex-1), 2^ex) */
+    int e = ex - 1;
+    if (e < -126) e = -126;           /* subnormals share the lowest binade's spacing */
+    double q = ldexp(1.0, e - 7);     /* spacing of representable values here */
+    double n = nearbyint(a / q);      /* exact quotient; default mode = ties-to-even */
+    double r = n * q;
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80;
+    float f = (float)r;               /* exact: r has at most 8 significant bits */
+    uint32_t bits;
+    memcpy(&bits, &f, 4);
+    return (uint16_t)(sign | (uint16_t)(bits >> 16));
+}
+
+double orc_bf16_to_double(uint16_t b) {
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+/* OCP fp8 e4m3 ("fn"): 1 sign, 4 exponent (bias 7), 3 fraction bits; no
+ * infinities; S.1111.111 is NaN; largest finite 448; subnormals m/8 * 2^-6. */
+double orc_e4m3_to_double(uint8_t c) {
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Nearest e4m3 value, ties to even, magnitudes beyond 448 saturate to 448. */
+uint8_t orc_e4m3_from_double_sat(double v) {
+    if (isnan(v)) return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    if (a == 0.0) return sign;
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;
+    if (e < -6) e = -6;
+    double q = ldexp(1.0, e - 3);
+    double r = nearbyint(a / q) * q;  /* <= 448 because 448 is representable */
+    if (r == 0.0) return sign;
+    frexp(r, &ex);
+    e = ex - 1;
+    uint8_t code;
+    if (e >= -6) {
+        double frac = r / ldexp(1.0, e) - 1.0;          /* in [0, 1) in steps of 1/8 */
+        code = (uint8_t)(((e + 7) << 3) | (int)(frac * 8.0));
+    } else {
+        code = (uint8_t)(r / ldexp(1.0, -9));           /* subnormal: multiple of 2^-9 */
+    }
+    return (uint8_t)(sign | code);
+}
+
+/* ------------------------------------------------------------------------ */
+/* host helpers whose values the pages print                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Size of one rank's routing payload: a Boolean map holds one byte per
+ * (token, expert); dense top-k indices hold one int16 per (token, slot).
+ * [P2] section "Memory impact". */
+int64_t orc_routing_bytes(int64_t tokens, int64_t experts, int64_t topk, int32_t fmt) {
+    if (fmt == ORC_SPARSE_U8) return tokens * experts;
+    if (fmt == ORC_DENSE_I16) return tokens * topk * 2;
+    return tokens * topk * 4;
+}
+
+/* Static output bound from a calibrated row count: rows x factor rounded up,
+ * then up to a multiple of 4.  [P3] section "What does this PR do ?" and the
+ * calibration figure under "Validation". */
+int64_t orc_capacity_from_rows(int64_t rows, double factor) {
+    double c = ceil((double)rows * factor);
+    int64_t ci = (int64_t)c;
+    return (ci + 3) / 4 * 4;
+}
+
+/* Largest row count the padded segments can need: every expert's segment is
+ * at most roundup(capacity, p) rows, and padding adds at most p-1 rows to each
+ * of the E segments on top of the T*K copies. */
+int64_t orc_out_rows_bound(int32_t T, int32_t E, int32_t K, int32_t pad, int32_t cap) {
+    int64_t by_copies = (int64_t)T * K + (int64_t)E * (pad - 1);
+    if (cap < 0) return by_copies;
+    int64_t per = ((int64_t)cap + pad - 1) / pad * pad;
+    int64_t by_cap = per * E;
+    return by_cap < by_copies ? by_cap : by_copies;
+}
+
+/* ------------------------------------------------------------------------ */
+/* routing metadata: counts, capacity, padding, offsets, row map, flag       */
+/* ------------------------------------------------------------------------ */
+/*
+ * Inputs: T tokens (only t < T_live are routed), E experts, K slots, routing
+ * as dense indices [T,K] (int16 or int32, -1 = empty slot) or a Boolean map
+ * [T,E]; optional probabilities with the routing's shape; padding multiple
+ * pad >= 1; per-expert capacity cap (< 0 = none); R rows in the output.
+ *   [P2] "Memory impact" / "Implementation": the two routing formats.
+ *   [P2] "Output and gradient regression": per-expert counts, handle metadata,
+ *        optional probabilities.
+ *   [P2] "Full HybridEP reference validation": padding multiple.
+ *   [P3] "What does this PR do ?", "Validation": static output bound, device
+ *        counts, overflow flag, silent truncation.
+ *   [P4] "Motivation": the layout is inferred from the top-k indices.
+ *
+ * Readings where the pages are silent:
+ *   - copies are taken in canonical order: token ascending, then dense slot
+ *     ascending, or for the Boolean map expert ascending (slot j = rank of the
+ *     expert among the row's routed experts);
+ *   - dense entries outside [-1,E) and repeated experts in a row are skipped and
+ *     flagged; a Boolean row with more than K experts keeps the K lowest ids;
+ *   - counts are raw (before capacity and padding);
+ *   - an expert keeps its first min(count, cap) copies in canonical order;
+ *     count == cap is not an overflow;
+ *   - a segment is the kept copies padded up to a multiple of pad; segments
+ *     follow each other in expert order; rows inside a segment follow token
+ *     order; copies whose row would fall at or beyond R are dropped;
+ *   - rows that hold no copy have src_row = -1 and perm_prob = 0.
+ * Outputs: counts[E], seg_off[E+1], row_id[T*K], copy_prob[T*K],
+ * copy_expert[T*K] (expert of each slot or -1), src_row[R], perm_prob[R],
+ * *rows_needed, *flag.
+ */
+int orc_route(int32_t T, int32_t E, int32_t K, int32_t fmt, const void* routing,
+              const float* probs, int32_t pad, int32_t cap, int64_t R, int32_t T_live,
+              int32_t* counts, int64_t* seg_off, int32_t* row_id, float* copy_prob,
+              int32_t* copy_expert, int32_t* src_row, float* perm_prob,
+              int64_t* rows_needed, int32_t* flag) {
+    if (T < 0 || E < 1 || K < 1 || pad < 1 || R < 0) return -1;
+    if (T_live < 0 || T_live > T) T_live = T;
+    int32_t f = 0;
+    uint8_t* seen = (uint8_t*)calloc((size_t)E, 1);
+    int64_t* next = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    int32_t* kept = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    if (!seen || !next || !kept) { free(seen); free(next); free(kept); return -2; }
+
+    /* 1. canonical copies */
+    for (int64_t i = 0; i < (int64_t)T * K; i++) { copy_expert[i] = -1; copy_prob[i] = 0.0f; }
+    for (int32_t t = 0; t < T_live; t++) {
+        if (fmt == ORC_SPARSE_U8) {
+            const uint8_t* map = (const uint8_t*)routing + (int64_t)t * E;
+            int32_t j = 0;
+            for (int32_t e = 0; e < E; e++) {
+                if (!map[e]) continue;
+                if (j >= K) { f |= ORC_FLAG_DUPLICATE; continue; }
+                copy_expert[(int64_t)t * K + j] = e;
+                copy_prob[(int64_t)t * K + j] = probs ? probs[(int64_t)t * E + e] : 1.0f;
+                j++;
+            }
+        } else {
+            memset(seen, 0, (size_t)E);
+            for (int32_t j = 0; j < K; j++) {
+                int64_t at = (int64_t)t * K + j;
+                int32_t e = (fmt == ORC_DENSE_I16) ? ((const int16_t*)routing)[at]
+                                                   : ((const int32_t*)routing)[at];
+                if (e == -1) continue;
+                if (e < -1 || e >= E) { f |= ORC_FLAG_BAD_EXPERT; continue; }
+                if (seen[e]) { f |= ORC_FLAG_DUPLICATE; continue; }
+                seen[e] = 1;
+                copy_expert[at] = e;
+                copy_prob[at] = probs ? probs[at] : 1.0f;
+            }
+        }
+    }
+
+    /* 2. raw counts */
+    for (int32_t e = 0; e < E; e++) counts[e] = 0;
+    for (int64_t i = 0; i < (int64_t)T * K; i++)
+        if (copy_expert[i] >= 0) counts[copy_expert[i]]++;
+
+    /* 3. capacity */
+    for (int32_t e = 0; e < E; e++) {
+        kept[e] = counts[e];
+        if (cap >= 0 && counts[e] > cap) { kept[e] = cap; f |= ORC_FLAG_CAPACITY; }
+    }
+
+    /* 4. padding and exclusive scan over experts */
+    seg_off[0] = 0;
+    for (int32_t e = 0; e < E; e++) {
+        int64_t padded = ((int64_t)kept[e] + pad - 1) / pad * pad;
+        seg_off[e + 1] = seg_off[e] + padded;
+    }
+    *rows_needed = seg_off[E];
+    if (seg_off[E] > R) f |= ORC_FLAG_OUT_ROWS;
+
+    /* 5. row assignment */
+    for (int64_t r = 0; r < R; r++) { src_row[r] = -1; perm_prob[r] = 0.0f; }
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t j = 0; j < K; j++) {
+            int64_t at = (int64_t)t * K + j;
+            int32_t e = copy_expert[at];
+            row_id[at] = -1;
+            if (e < 0) continue;
+            int64_t rank = next[e]++;
+            int64_t row = seg_off[e] + rank;
+            if (rank < kept[e] && row < R) {
+                row_id[at] = (int32_t)row;
+                src_row[row] = t;
+                perm_prob[row] = copy_prob[at];
+            } else {
+                copy_prob[at] = 0.0f;
+            }
+        }
+    }
+    *flag = f;
+    free(seen); free(next); free(kept);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* permute: copy each kept token row to its destination row                  */
+/* [P1] "Summary"/"Configuration": dispatch writes permuted tokens into a      */
+/* caller-provided output; [P2] "Full HybridEP reference validation":         */
+/* dispatch with permutation, BF16 and FP8 payloads.                          */
+/* Rows are opaque byte strings (a bf16 row, an fp8 row, or its scale row).   */
+/* ------------------------------------------------------------------------ */
+void orc_permute_rows(int32_t T, int32_t K, int64_t row_bytes, const uint8_t* x,
+                      const int32_t* row_id, uint8_t* out) {
+    for (int32_t t = 0; t < T; t++)
+        for (int32_t j = 0; j < K; j++) {
+            int32_t r = row_id[(int64_t)t * K + j];
+            if (r >= 0) memcpy(out + (int64_t)r * row_bytes, x + (int64_t)t * row_bytes, (size_t)row_bytes);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* combine: probability-weighted sum of each token's surviving copies         */
+/* [P1] "Summary"/"Motivation": combine with unpermute is the final read of   */
+/* the expert output; [P5] review-fix commit: the top-k reduction of a token  */
+/* set that may be empty.  Sum in double, one rounding to bf16; a token with  */
+/* no surviving copy yields 0.                                               */
+/* ------------------------------------------------------------------------ */
+void orc_combine_bf16(int32_t T, int32_t K, int32_t H, const int32_t* row_id,
+                      const float* copy_prob, int32_t apply_probs, const uint16_t* Y,
+                      uint16_t* y) {
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t h = 0; h < H; h++) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < K; j++) {
+                int32_t r = row_id[(int64_t)t * K + j];
+                if (r < 0) continue;
+                double w = apply_probs ? (double)copy_prob[(int64_t)t * K + j] : 1.0;
+                acc += w * orc_bf16_to_double(Y[(int64_t)r * H + h]);
+            }
+            y[(int64_t)t * H + h] = orc_bf16_from_double(acc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* expert MLP (bf16 weights)                                                 */
+/* [P1] "Summary"/"Configuration": a grouped FC1 -> activation -> FC2 MLP     */
+/* writing FC2 into a caller-owned buffer; [P5] streaming-load commit: FC1    */
+/* weight is the concatenated w3_w1 matrix.                                  */
+/* Reading: W1 is [2F, H] with rows [0,F) the gate (SiLU) half and [F,2F) the  */
+/* up half; W2 is [H, F]; a = bf16(silu(g) * u); y = bf16(W2 a); sums and     */
+/* silu in double; silu(z) = z / (1 + exp(-z)).                              */
+/* ------------------------------------------------------------------------ */
+static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+void orc_expert_mlp_bf16(int32_t n, int32_t H, int32_t F, const uint16_t* x,
+                         const uint16_t* w1, const uint16_t* w2, uint16_t* y,
+                         uint16_t* a_out /* nullable [n,F] */) {
+#pragma omp parallel
+    {
+        uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
+#pragma omp for schedule(dynamic)
+        for (int32_t r = 0; r < n; r++) {
+            const uint16_t* xr = x + (int64_t)r * H;
+            for (int32_t i = 0; i < F; i++) {
+                const uint16_t* wg = w1 + (int64_t)i * H;
+                const uint16_t* wu = w1 + (int64_t)(F + i) * H;
+                double g = 0.0, u = 0.0;
+                for (int32_t h = 0; h < H; h++) {
+                    double xv = orc_bf16_to_double(xr[h]);
+                    g += xv * orc_bf16_to_double(wg[h]);
+                    u += xv * orc_bf16_to_double(wu[h]);
+                }
+                a[i] = orc_bf16_from_double(orc_silu(g) * u);
+            }
+            if (a_out) memcpy(a_out + (int64_t)r * F, a, sizeof(uint16_t) * (size_t)F);
+            for (int32_t o = 0; o < H; o++) {
+                const uint16_t* w = w2 + (int64_t)o * F;
+                double acc = 0.0;
+                for (int32_t i = 0; i < F; i++)
+                    acc += orc_bf16_to_double(a[i]) * orc_bf16_to_double(w[i]);
+                y[(int64_t)r * H + o] = orc_bf16_from_double(acc);
+            }
+        }
+        free(a);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp8 block quantisation of activation rows                                 */
+/* [P2] "Full HybridEP reference validation" and [P1] "Configuration": FP8    */
+/* payloads and FP8 expert GEMMs.  The pages do not fix the scaling; reading: */
+/* one fp32 scale per (row, 128 columns), scale = block amax / 448 (1 for an  */
+/* all-zero block), code = e4m3(x / scale) saturating.  Scale and quotient    */
+/* are float operations (they decide the integer code).                       */
+/* ------------------------------------------------------------------------ */
+void orc_quant_rows_e4m3_f32(int32_t n, int32_t cols, const float* x, uint8_t* q, float* scales) {
+    int32_t nb = cols / 128;
+    for (int32_t r = 0; r < n; r++)
+        for (int32_t b = 0; b < nb; b++) {
+            const float* xb = x + (int64_t)r * cols + (int64_t)b * 128;
+            float amax = 0.0f;
+            for (int32_t i = 0; i < 128; i++) {
+                float v = fabsf(xb[i]);
+                if (v > amax) amax = v;
+            }
+            float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scales[(int64_t)r * nb + b] = s;
+            for (int32_t i = 0; i < 128; i++) {
+                float v = xb[i] / s;
+                q[(int64_t)r * cols + (int64_t)b * 128 + i] = orc_e4m3_from_double_sat((double)v);
+            }
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* expert MLP with fp8 weights (W8A8)                                        */
+/* [P5] first and streaming-load commits: low-precision expert weights with   */
+/* block scales.  Readings: weights are e4m3 codes with one fp32 scale per    */
+/* 128x128 block; the bf16 input row is quantised per 1x128 block (above);     */
+/* products use dequantised values (code * scale, exact in double); a =       */
+/* silu(g)*u is re-quantised per 1x128 block (decision in float) before FC2;  */
+/* FC2 output is bf16.                                                        */
+/* ------------------------------------------------------------------------ */
+void orc_expert_mlp_fp8(int32_t n, int32_t H, int32_t F, const uint16_t* x,
+                        const uint8_t* w1q, const float* w1s, const uint8_t* w2q,
+                        const float* w2s, uint16_t* y) {
+    int32_t hb = H / 128, fb = F / 128;
+#pragma omp parallel
+    {
+        float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+        uint8_t* xq = (uint8_t*)malloc((size_t)H);
+        float* xs = (float*)malloc(sizeof(float) * (size_t)hb);
+        double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+        float* af = (float*)malloc(sizeof(float) * (size_t)F);
+        uint8_t* aq = (uint8_t*)malloc((size_t)F);
+        float* as = (float*)malloc(sizeof(float) * (size_t)fb);
+        double* ad = (double*)malloc(sizeof(double) * (size_t)F);
+#pragma omp for schedule(dynamic)
+        for (int32_t r = 0; r < n; r++) {
+            for (int32_t h = 0; h < H; h++) xf[h] = (float)orc_bf16_to_double(x[(int64_t)r * H + h]);
+            orc_quant_rows_e4m3_f32(1, H, xf, xq, xs);
+            for (int32_t h = 0; h < H; h++) xd[h] = orc_e4m3_to_double(xq[h]) * (double)xs[h / 128];
+            for (int32_t i = 0; i < F; i++) {
+                double g = 0.0, u = 0.0;
+                for (int32_t h = 0; h < H; h++) {
+                    double wg = orc_e4m3_to_double(w1q[(int64_t)i * H + h]) *
+                                (double)w1s[(int64_t)(i / 128) * hb + h / 128];
+                    double wu = orc_e4m3_to_double(w1q[(int64_t)(F + i) * H + h]) *
+                                (double)w1s[(int64_t)((F + i) / 128) * hb + h / 128];
+                    g += xd[h] * wg;
+                    u += xd[h] * wu;
+                }
+                af[i] = (float)(orc_silu(g) * u);
+            }
+            orc_quant_rows_e4m3_f32(1, F, af, aq, as);
+            for (int32_t i = 0; i < F; i++) ad[i] = orc_e4m3_to_double(aq[i]) * (double)as[i / 128];
+            for (int32_t o = 0; o < H; o++) {
+                double acc = 0.0;
+                for (int32_t i = 0; i < F; i++)
+                    acc += ad[i] * orc_e4m3_to_double(w2q[(int64_t)o * F + i]) *
+                           (double)w2s[(int64_t)(o / 128) * fb + i / 128];
+                y[(int64_t)r * H + o] = orc_bf16_from_double(acc);
+            }
+        }
+        free(xf); free(xq); free(xs); free(xd); free(af); free(aq); free(as); free(ad);
+    }
+}
