@@ -1,0 +1,252 @@
+"""torch-facing binding of the C ABI (argument marshalling only).
+
+torch supplies device memory and the current HIP stream; every computation
+is a kernel of libmoe_route.so.  Shapes are fixed per ``Dispatcher`` (the
+handle is initialised once, like a static-shape buffer), and no call reads a
+device value back to the host.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import torch
+
+from . import _abi as A
+
+_FMT = {"dense_i16": A.ROUTE_DENSE_I16, "dense_i32": A.ROUTE_DENSE_I32, "sparse_bool": A.ROUTE_SPARSE_BOOL}
+_FMT_DTYPES = {A.ROUTE_DENSE_I16: (torch.int16,), A.ROUTE_DENSE_I32: (torch.int32,),
+               A.ROUTE_SPARSE_BOOL: (torch.uint8, torch.bool, torch.int8)}
+_DT = {"bf16": A.BF16, "fp8": A.FP8E4M3_B128}
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def make_desc(T: int, H: int, E: int, K: int, route_fmt: str = "dense_i16", payload: str = "bf16",
+              pad_multiple: int = 1, capacity: Optional[int] = None, out_rows: int = 0) -> A.MoeDesc:
+    return A.MoeDesc(T=T, H=H, E=E, K=K, route_fmt=_FMT[route_fmt], payload=_DT[payload],
+                     pad_multiple=pad_multiple, capacity=-1 if capacity is None else int(capacity),
+                     out_rows=int(out_rows))
+
+
+def out_rows_bound(T: int, H: int, E: int, K: int, pad_multiple: int = 1, capacity: Optional[int] = None,
+                   route_fmt: str = "dense_i16", payload: str = "bf16") -> int:
+    d = make_desc(T, H, E, K, route_fmt, payload, pad_multiple, capacity)
+    return int(A.lib().moe_out_rows_bound(C.byref(d)))
+
+
+def routing_bytes(T: int, E: int, K: int, route_fmt: str = "dense_i16") -> int:
+    d = make_desc(T, 8, E, K, route_fmt)
+    return int(A.lib().moe_routing_bytes(C.byref(d)))
+
+
+def capacity_from_rows(rows: int, factor: float) -> int:
+    return int(A.lib().moe_capacity_from_rows(int(rows), float(factor)))
+
+
+def assert_no_overflow(flag: torch.Tensor) -> None:
+    """Device-side assert that the overflow flag is clear; the host does not
+    wait for it (the failure surfaces at the next synchronisation)."""
+    torch._assert_async(flag[0] == 0)
+
+
+class Dispatcher:
+    """One fixed-shape dispatch/MLP/combine problem with its workspace."""
+
+    def __init__(self, T: int, H: int, E: int, K: int, *, route_fmt: str = "dense_i16",
+                 payload: str = "bf16", pad_multiple: int = 1, capacity: Optional[int] = None,
+                 out_rows: int = 0, device=None):
+        L = A.lib()
+        self.device = torch.device(device if device is not None else "cuda")
+        self.desc = make_desc(T, H, E, K, route_fmt, payload, pad_multiple, capacity, out_rows)
+        ws_bytes = int(L.moe_workspace_bytes(C.byref(self.desc)))
+        if ws_bytes == 0:
+            raise A.MoeError(A.MOE_ESHAPE, "moe_workspace_bytes")
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        self.h = A.MoeHandle()
+        A.check(L.moe_handle_init(C.byref(self.desc), _ptr(self.ws), ws_bytes, C.byref(self.h)), "moe_handle_init")
+        self.T, self.H, self.E, self.K = T, H, E, K
+        self.R = int(self.h.desc.out_rows)
+        self.route_fmt = self.desc.route_fmt
+        self.payload = self.desc.payload
+        self.tokens_per_expert = torch.empty(E, dtype=torch.int32, device=self.device)
+        self.flag = torch.empty(1, dtype=torch.int32, device=self.device)
+
+    # ---- views of the handle's device metadata ------------------------------
+    def _view(self, field: str, dtype: torch.dtype, n: int) -> torch.Tensor:
+        off = int(getattr(self.h, field)) - int(self.h.ws)
+        nb = n * torch.empty(0, dtype=dtype).element_size()
+        return self.ws[off:off + nb].view(dtype)
+
+    @property
+    def row_id(self):
+        return self._view("row_id", torch.int32, self.T * self.K).view(self.T, self.K)
+
+    @property
+    def copy_prob(self):
+        return self._view("copy_prob", torch.float32, self.T * self.K).view(self.T, self.K)
+
+    @property
+    def seg_off(self):
+        return self._view("seg_off", torch.int64, self.E + 1)
+
+    @property
+    def kept(self):
+        return self._view("kept", torch.int32, self.E)
+
+    @property
+    def src_row(self):
+        return self._view("src_row", torch.int32, self.R)
+
+    @property
+    def rows_needed(self):
+        return self._view("rows_needed", torch.int64, 1)
+
+    # ---- checks ------------------------------------------------------------------
+    def _dev(self, t: torch.Tensor, name: str):
+        _need(t.device == self.device or (t.device.type == "cuda" and self.device.type == "cuda"
+                                          and t.device.index == torch.cuda.current_device()),
+              f"{name} must live on {self.device}")
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+
+    def _check_routing(self, routing, probs, T_live):
+        self._dev(routing, "routing")
+        _need(routing.dtype in _FMT_DTYPES[self.route_fmt], f"routing dtype {routing.dtype} does not match the format")
+        shape = (self.T, self.E) if self.route_fmt == A.ROUTE_SPARSE_BOOL else (self.T, self.K)
+        _need(tuple(routing.shape) == shape, f"routing shape {tuple(routing.shape)} != {shape}")
+        if probs is not None:
+            self._dev(probs, "probs")
+            _need(probs.dtype == torch.float32 and tuple(probs.shape) == shape, "probs must be float32 shaped like routing")
+        if T_live is not None:
+            self._dev(T_live, "T_live")
+            _need(T_live.dtype == torch.int32 and T_live.numel() == 1, "T_live must be one int32")
+
+    # ---- calls -------------------------------------------------------------------
+    def preprocess(self, routing: torch.Tensor, probs: Optional[torch.Tensor] = None,
+                   T_live: Optional[torch.Tensor] = None, out_probs: Optional[torch.Tensor] = None):
+        self._check_routing(routing, probs, T_live)
+        if out_probs is not None:
+            self._dev(out_probs, "out_probs")
+            _need(out_probs.dtype == torch.float32 and out_probs.numel() >= self.R, "out_probs must hold R floats")
+        A.check(A.lib().moe_route_preprocess(C.byref(self.h), _ptr(routing), _ptr(probs), _ptr(T_live),
+                                             _ptr(self.tokens_per_expert), _ptr(out_probs), _ptr(self.flag),
+                                             _stream()), "moe_route_preprocess")
+        return self.tokens_per_expert, self.flag
+
+    def _alloc_out(self, x, out, x_scales, out_scales):
+        if out is None:
+            out = torch.empty((self.R, self.H), dtype=x.dtype, device=self.device)
+        self._dev(out, "out")
+        _need(out.dtype == x.dtype and tuple(out.shape) == (self.R, self.H), "out must be [R,H] like x")
+        if self.payload == A.FP8E4M3_B128:
+            _need(x_scales is not None, "fp8 payload needs x_scales")
+            self._dev(x_scales, "x_scales")
+            _need(x_scales.dtype == torch.float32 and tuple(x_scales.shape) == (self.T, self.H // 128),
+                  "x_scales must be float32 [T, H/128]")
+            if out_scales is None:
+                out_scales = torch.empty((self.R, self.H // 128), dtype=torch.float32, device=self.device)
+            self._dev(out_scales, "out_scales")
+            _need(tuple(out_scales.shape) == (self.R, self.H // 128), "out_scales must be [R, H/128]")
+        return out, out_scales
+
+    def _check_x(self, x):
+        self._dev(x, "x")
+        _need(tuple(x.shape) == (self.T, self.H), f"x shape {tuple(x.shape)} != {(self.T, self.H)}")
+        if self.payload == A.BF16:
+            _need(x.dtype == torch.bfloat16, "bf16 payload expects a bfloat16 x")
+        else:
+            _need(x.dtype in _FP8_DTYPES, "fp8 payload expects uint8 / float8_e4m3fn codes")
+
+    def permute(self, x: torch.Tensor, x_scales: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, out_scales: Optional[torch.Tensor] = None):
+        self._check_x(x)
+        out, out_scales = self._alloc_out(x, out, x_scales, out_scales)
+        A.check(A.lib().moe_permute(C.byref(self.h), _ptr(x), _ptr(x_scales), _ptr(out), _ptr(out_scales),
+                                    _stream()), "moe_permute")
+        return (out, out_scales) if self.payload == A.FP8E4M3_B128 else out
+
+    def dispatch(self, x: torch.Tensor, routing: torch.Tensor, probs: Optional[torch.Tensor] = None, *,
+                 x_scales=None, out=None, out_scales=None, out_probs=None, T_live=None):
+        """preprocess + permute.  Returns (permuted, tokens_per_expert, flag,
+        out_probs, out_scales); out_probs / out_scales are None unless given
+        / fp8."""
+        self._check_x(x)
+        self._check_routing(routing, probs, T_live)
+        out, out_scales = self._alloc_out(x, out, x_scales, out_scales)
+        if out_probs is not None:
+            self._dev(out_probs, "out_probs")
+            _need(out_probs.dtype == torch.float32 and out_probs.numel() >= self.R, "out_probs must hold R floats")
+        A.check(A.lib().moe_dispatch(C.byref(self.h), _ptr(routing), _ptr(probs), _ptr(T_live), _ptr(x),
+                                     _ptr(x_scales), _ptr(out), _ptr(out_scales), _ptr(out_probs),
+                                     _ptr(self.tokens_per_expert), _ptr(self.flag), _stream()), "moe_dispatch")
+        return out, self.tokens_per_expert, self.flag, out_probs, out_scales
+
+    def mlp_scratch_bytes(self, F: int, wdtype: str = "bf16") -> int:
+        return int(A.lib().moe_mlp_scratch_bytes(C.byref(self.h), int(F), _DT[wdtype]))
+
+    def alloc_mlp_scratch(self, F: int, wdtype: str = "bf16") -> torch.Tensor:
+        n = self.mlp_scratch_bytes(F, wdtype)
+        _need(n > 0, "invalid F / wdtype for the MLP scratch")
+        return torch.empty(n, dtype=torch.uint8, device=self.device)
+
+    def grouped_mlp(self, perm: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, *,
+                    w1_scales: Optional[torch.Tensor] = None, w2_scales: Optional[torch.Tensor] = None,
+                    scratch: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+        """Grouped SwiGLU MLP over the permuted rows.  w1 [E,2F,H], w2 [E,H,F]
+        (bf16, or e4m3 codes with 128x128 block scales)."""
+        fp8w = w1.dtype in _FP8_DTYPES
+        wdtype = "fp8" if fp8w else "bf16"
+        E, F2, H = w1.shape
+        F = F2 // 2
+        _need(E == self.E and H == self.H and tuple(w2.shape) == (self.E, self.H, F), "weight shapes")
+        for t, n in ((perm, "perm"), (w1, "w1"), (w2, "w2")):
+            self._dev(t, n)
+        _need(perm.dtype == torch.bfloat16 and tuple(perm.shape) == (self.R, self.H), "perm must be bf16 [R,H]")
+        if fp8w:
+            _need(w1_scales is not None and w2_scales is not None, "fp8 weights need block scales")
+            _need(tuple(w1_scales.shape) == (E, F2 // 128, H // 128) and tuple(w2_scales.shape) == (E, H // 128, F // 128),
+                  "block-scale shapes")
+        else:
+            _need(w1.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16, "bf16 weights expected")
+        if scratch is None:
+            scratch = self.alloc_mlp_scratch(F, wdtype)
+        if out is None:
+            out = torch.empty((self.R, self.H), dtype=torch.bfloat16, device=self.device)
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.R, self.H), "out must be bf16 [R,H]")
+        A.check(A.lib().moe_grouped_swiglu_mlp(C.byref(self.h), F, _DT[wdtype], _ptr(perm), None, _ptr(w1),
+                                               _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(scratch),
+                                               scratch.numel(), _ptr(out), _stream()), "moe_grouped_swiglu_mlp")
+        return out
+
+    def combine(self, expert_out: torch.Tensor, apply_probs: bool = True, out: Optional[torch.Tensor] = None):
+        self._dev(expert_out, "expert_out")
+        _need(expert_out.dtype == torch.bfloat16 and tuple(expert_out.shape) == (self.R, self.H),
+              "expert_out must be bf16 [R,H]")
+        if out is None:
+            out = torch.empty((self.T, self.H), dtype=torch.bfloat16, device=self.device)
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.T, self.H), "out must be bf16 [T,H]")
+        A.check(A.lib().moe_combine(C.byref(self.h), _ptr(expert_out), 1 if apply_probs else 0, _ptr(out),
+                                    _stream()), "moe_combine")
+        return out
+
+    def layer(self, x, routing, probs, w1, w2, *, perm=None, scratch=None, expert_out=None, out=None,
+              w1_scales=None, w2_scales=None, T_live=None, apply_probs=True):
+        """dispatch -> grouped MLP -> combine on the current stream."""
+        perm, _, flag, _, _ = self.dispatch(x, routing, probs, out=perm, T_live=T_live)
+        y = self.grouped_mlp(perm, w1, w2, w1_scales=w1_scales, w2_scales=w2_scales, scratch=scratch,
+                             out=expert_out)
+        return self.combine(y, apply_probs=apply_probs, out=out)

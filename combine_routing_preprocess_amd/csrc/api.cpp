@@ -1,0 +1,271 @@
+// extern "C" entry points of libmoe_route (declared in include/moe_route.h):
+// host-side validation, workspace carving, stale-handle detection and the
+// kernel launches.  Nothing here synchronises with the device or allocates
+// device memory.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+std::mutex g_mu;
+std::unordered_map<uintptr_t, uint64_t> g_epoch;   // workspace address -> generation
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int check_desc(const moe_desc* d) {
+    if (!d) return MOE_EINVAL;
+    if (d->route_fmt < MOE_ROUTE_DENSE_I16 || d->route_fmt > MOE_ROUTE_SPARSE_BOOL) return MOE_EINVAL;
+    if (d->payload != MOE_BF16 && d->payload != MOE_FP8E4M3_B128) return MOE_EDTYPE;
+    if (d->T < 0 || d->E < 1 || d->E > kMaxE || d->K < 1 || d->K > kMaxE || d->pad_multiple < 1 || d->H < 1)
+        return MOE_ESHAPE;
+    if (d->payload == MOE_BF16 && d->H % 8) return MOE_ESHAPE;
+    if (d->payload == MOE_FP8E4M3_B128 && d->H % 128) return MOE_ESHAPE;
+    if ((int64_t)d->T * d->K > INT32_MAX) return MOE_ESHAPE;
+    if (d->out_rows < 0 || d->out_rows > INT32_MAX) return MOE_ESHAPE;
+    return MOE_OK;
+}
+
+int64_t bound_rows(const moe_desc* d) {
+    const int64_t p = d->pad_multiple;
+    const int64_t by_copies = (int64_t)d->T * d->K + (int64_t)d->E * (p - 1);
+    if (d->capacity < 0) return by_copies;
+    const int64_t by_cap = ((int64_t)d->capacity + p - 1) / p * p * d->E;
+    return by_cap < by_copies ? by_cap : by_copies;
+}
+
+struct Layout {
+    size_t mask, base, err, seg, kept, rn, rowid, cp, src, total;
+    int n_tiles;
+    int64_t R;
+};
+
+int make_layout(const moe_desc* d, Layout* L) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    const int64_t R = d->out_rows ? d->out_rows : bound_rows(d);
+    if (R > INT32_MAX) return MOE_ESHAPE;
+    L->R = R;
+    L->n_tiles = (d->T + kTileTok - 1) / kTileTok;
+    const size_t nt = (size_t)L->n_tiles, E = (size_t)d->E, TK = (size_t)d->T * d->K;
+    size_t o = 0;
+    L->mask = o;  o = up(o + nt * E * 8, kAlign);
+    L->base = o;  o = up(o + nt * E * 4, kAlign);
+    L->err = o;   o = up(o + nt * 4, kAlign);
+    L->seg = o;   o = up(o + (E + 1) * 8, kAlign);
+    L->kept = o;  o = up(o + E * 4, kAlign);
+    L->rn = o;    o = up(o + 8, kAlign);
+    L->rowid = o; o = up(o + TK * 4, kAlign);
+    L->cp = o;    o = up(o + TK * 4, kAlign);
+    L->src = o;   o = up(o + (size_t)R * 4, kAlign);
+    L->total = o;
+    return MOE_OK;
+}
+
+int check_handle(const moe_handle* h, bool need_routing) {
+    if (!h) return MOE_EINVAL;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_epoch.find((uintptr_t)h->ws);
+        if (it == g_epoch.end() || it->second != h->epoch) return MOE_ESTALE;
+    }
+    if (need_routing && h->state < 1) return MOE_ESTALE;
+    return MOE_OK;
+}
+
+int num_cu() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    if (dev < 64) cache[dev] = n;
+    return n;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument (null pointer or unknown enum)";
+        case MOE_ESHAPE: return "shape outside the supported range";
+        case MOE_EDTYPE: return "unsupported dtype or format";
+        case MOE_EALIGN: return "device pointer not 16-byte aligned";
+        case MOE_ESTALE: return "stale handle (workspace re-initialised or no routing metadata)";
+        case MOE_EHIP: return "HIP runtime error";
+        case MOE_EUNSUPPORTED: return "not supported";
+        case MOE_ENOSPC: return "workspace or scratch too small";
+        default: return "unknown status";
+    }
+}
+
+int64_t moe_out_rows_bound(const moe_desc* desc) {
+    if (check_desc(desc)) return -1;
+    return bound_rows(desc);
+}
+
+int64_t moe_routing_bytes(const moe_desc* desc) {
+    if (check_desc(desc)) return -1;
+    if (desc->route_fmt == MOE_ROUTE_SPARSE_BOOL) return (int64_t)desc->T * desc->E;
+    return (int64_t)desc->T * desc->K * (desc->route_fmt == MOE_ROUTE_DENSE_I16 ? 2 : 4);
+}
+
+int64_t moe_capacity_from_rows(int64_t rows, double factor) {
+    if (rows < 0 || !(factor > 0.0)) return -1;
+    const double c = std::ceil((double)rows * factor);
+    if (c > (double)INT64_MAX / 2) return -1;
+    const int64_t ci = (int64_t)c;
+    return (ci + 3) / 4 * 4;
+}
+
+size_t moe_workspace_bytes(const moe_desc* desc) {
+    Layout L;
+    if (make_layout(desc, &L)) return 0;
+    return L.total;
+}
+
+int moe_handle_init(const moe_desc* desc, void* d_ws, size_t ws_bytes, moe_handle* h) {
+    if (!h) return MOE_EINVAL;
+    Layout L;
+    int rc = make_layout(desc, &L);
+    if (rc) return rc;
+    if (!d_ws) return MOE_EINVAL;
+    if (!al16(d_ws)) return MOE_EALIGN;
+    if (ws_bytes < L.total) return MOE_ENOSPC;
+    std::memset(h, 0, sizeof(*h));
+    h->desc = *desc;
+    h->desc.out_rows = L.R;
+    h->n_tiles = L.n_tiles;
+    h->ws = d_ws;
+    h->ws_bytes = ws_bytes;
+    char* b = (char*)d_ws;
+    h->tile_mask = (uint64_t*)(b + L.mask);
+    h->tile_base = (int32_t*)(b + L.base);
+    h->tile_err = (int32_t*)(b + L.err);
+    h->seg_off = (int64_t*)(b + L.seg);
+    h->kept = (int32_t*)(b + L.kept);
+    h->rows_needed = (int64_t*)(b + L.rn);
+    h->row_id = (int32_t*)(b + L.rowid);
+    h->copy_prob = (float*)(b + L.cp);
+    h->src_row = (int32_t*)(b + L.src);
+    std::lock_guard<std::mutex> lk(g_mu);
+    h->epoch = ++g_epoch[(uintptr_t)d_ws];
+    return MOE_OK;
+}
+
+int moe_route_preprocess(moe_handle* h, const void* d_routing, const float* d_probs,
+                         const int32_t* d_T_live, int32_t* d_tokens_per_expert, float* d_out_probs,
+                         int32_t* d_flag, void* stream) {
+    int rc = check_handle(h, false);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (!d_tokens_per_expert || !d_flag) return MOE_EINVAL;
+    if (d.T > 0 && !d_routing) return MOE_EINVAL;
+    if (d_routing && !al16(d_routing)) return MOE_EALIGN;
+    if ((d_probs && !al4(d_probs)) || (d_out_probs && !al4(d_out_probs)) || !al4(d_tokens_per_expert) ||
+        !al4(d_flag) || (d_T_live && !al4(d_T_live)))
+        return MOE_EALIGN;
+    rc = hip_rc(launch_route(h, d_routing, d_probs, d_T_live, d_tokens_per_expert, d_out_probs, d_flag,
+                             (hipStream_t)stream));
+    if (rc == MOE_OK) h->state = 1;
+    return rc;
+}
+
+int moe_permute(const moe_handle* h, const void* d_x, const float* d_x_scales, void* d_out,
+                float* d_out_scales, void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    const bool fp8 = d.payload == MOE_FP8E4M3_B128;
+    if (d.T > 0 && (!d_x || !d_out)) return MOE_EINVAL;
+    if (fp8 && d.T > 0 && (!d_x_scales || !d_out_scales)) return MOE_EINVAL;
+    if (!fp8 && (d_x_scales || d_out_scales)) return MOE_EDTYPE;
+    if ((d_x && !al16(d_x)) || (d_out && !al16(d_out))) return MOE_EALIGN;
+    if ((d_x_scales && !al4(d_x_scales)) || (d_out_scales && !al4(d_out_scales))) return MOE_EALIGN;
+    return hip_rc(launch_permute(h, d_x, d_x_scales, d_out, d_out_scales, (hipStream_t)stream));
+}
+
+int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs, const int32_t* d_T_live,
+                 const void* d_x, const float* d_x_scales, void* d_out, float* d_out_scales,
+                 float* d_out_probs, int32_t* d_tokens_per_expert, int32_t* d_flag, void* stream) {
+    int rc = check_handle(h, false);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    const bool fp8 = d.payload == MOE_FP8E4M3_B128;
+    // argument checks of the permute half before anything is enqueued
+    if (d.T > 0 && (!d_x || !d_out)) return MOE_EINVAL;
+    if (fp8 && d.T > 0 && (!d_x_scales || !d_out_scales)) return MOE_EINVAL;
+    if (!fp8 && (d_x_scales || d_out_scales)) return MOE_EDTYPE;
+    if ((d_x && !al16(d_x)) || (d_out && !al16(d_out))) return MOE_EALIGN;
+    rc = moe_route_preprocess(h, d_routing, d_probs, d_T_live, d_tokens_per_expert, d_out_probs, d_flag, stream);
+    if (rc) return rc;
+    return moe_permute(h, d_x, d_x_scales, d_out, d_out_scales, stream);
+}
+
+size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype) {
+    if (!h || F <= 0) return 0;
+    const size_t R = (size_t)h->desc.out_rows;
+    if (wdtype == MOE_BF16) return up(R * (size_t)F * 2, kAlign);
+    if (wdtype == MOE_FP8E4M3_B128) {
+        if (F % 128) return 0;
+        return up(R * (size_t)F, kAlign) + up(R * (size_t)(F / 128) * 4, kAlign);
+    }
+    return 0;
+}
+
+int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
+                           const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
+                           const void* d_w2, const float* d_w2_scales, void* d_scratch,
+                           size_t scratch_bytes, void* d_expert_out, void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (F <= 0) return MOE_ESHAPE;
+    if (d.payload != MOE_BF16 || d_perm_scales) return MOE_EDTYPE;
+    if (!d_perm || !d_w1 || !d_w2 || !d_expert_out || !d_scratch) return MOE_EINVAL;
+    if (!al16(d_perm) || !al16(d_w1) || !al16(d_w2) || !al16(d_expert_out) || !al16(d_scratch)) return MOE_EALIGN;
+    const size_t need = moe_mlp_scratch_bytes(h, F, wdtype);
+    if (need == 0) return MOE_ESHAPE;
+    if (scratch_bytes < need) return MOE_ENOSPC;
+    const int ncu = num_cu();
+    if (ncu <= 0) return MOE_EHIP;
+    if (wdtype == MOE_BF16) {
+        if (d_w1_scales || d_w2_scales) return MOE_EDTYPE;
+        if (d.H % 256 || F % 128) return MOE_ESHAPE;
+        return hip_rc(launch_mlp_bf16(h, F, d_perm, d_w1, d_w2, d_scratch, d_expert_out, ncu,
+                                      (hipStream_t)stream));
+    }
+    if (wdtype == MOE_FP8E4M3_B128) return MOE_EUNSUPPORTED;
+    return MOE_EDTYPE;
+}
+
+int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_probs, void* d_y,
+                void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (d.T > 0 && (!d_expert_out || !d_y)) return MOE_EINVAL;
+    if ((d_expert_out && !al16(d_expert_out)) || (d_y && !al16(d_y))) return MOE_EALIGN;
+    if (d.H % 8) return MOE_ESHAPE;
+    return hip_rc(launch_combine(h, d_expert_out, apply_probs ? 1 : 0, d_y, (hipStream_t)stream));
+}
+
+}  // extern "C"

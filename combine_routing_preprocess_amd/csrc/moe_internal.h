@@ -1,0 +1,40 @@
+// Internal declarations shared by the HIP translation units of libmoe_route.
+// Not part of the public ABI (that is include/moe_route.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_route.h"
+
+namespace moe {
+
+constexpr int kMaxE = 1024;      // experts supported by the routing kernels
+constexpr int kTileTok = 64;     // tokens per routing tile = one wavefront
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---- launchers (each returns a hipError_t) --------------------------------
+hipError_t launch_route(const moe_handle* h, const void* routing, const float* probs,
+                        const int32_t* T_live, int32_t* tokens_per_expert, float* out_probs,
+                        int32_t* flag, hipStream_t s);
+hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_scales, void* out,
+                          float* out_scales, hipStream_t s);
+hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs, void* y_out,
+                          hipStream_t s);
+hipError_t launch_mlp_bf16(const moe_handle* h, int F, const void* perm, const void* w1,
+                           const void* w2, void* act, void* expert_out, int num_cu, hipStream_t s);
+hipError_t launch_mlp_fp8(const moe_handle* h, int F, const void* perm, const void* w1,
+                          const float* w1s, const void* w2, const float* w2s, void* act,
+                          float* act_scales, void* expert_out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,73 @@
+// Dispatch-permute (K2): copy every kept token row to its destination rows.
+//
+// Operation: Megatron-LM PR #6800 "Reuse caller-owned HybridEP dispatch and
+// expert output buffers" (sections "Summary", "Configuration": permuted tokens
+// written into a caller-provided output buffer) and DeepEP PR #716 "perf:
+// reuse HybridEP routing allgather buffer" (section "Full HybridEP reference
+// validation": dispatch with permutation for BF16 and FP8 payloads).
+//
+// Token-major: one wavefront owns one token, reads its row once into
+// registers (16-byte loads) and stores it to each of its k destinations, so
+// HBM sees the algorithmic minimum, T row reads + (kept copies) row writes.
+// Row reads and writes bypass cache residency (non-temporal): the permuted
+// buffer is far larger than the last-level cache and is consumed by another
+// kernel.  fp8 rows carry their per-128-column fp32 scales along.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kPermU = 7;   // 16-byte chunks held per lane per pass
+
+__global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, int T, int K, int nch, int R,
+                                                 const int32_t* __restrict__ row_id,
+                                                 u32x4* __restrict__ out, const float* __restrict__ xs,
+                                                 float* __restrict__ outs, int nsc) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const u32x4* src = x + (size_t)t * nch;
+    const int32_t* rid = row_id + (size_t)t * K;
+    for (int c0 = 0; c0 < nch; c0 += 64 * kPermU) {
+        u32x4 v[kPermU];
+#pragma unroll
+        for (int u = 0; u < kPermU; ++u) {
+            const int c = c0 + u * 64 + lane;
+            if (c < nch) v[u] = __builtin_nontemporal_load(src + c);
+        }
+        for (int j = 0; j < K; ++j) {
+            const int r = rid[j];
+            if (r < 0 || r >= R) continue;
+            u32x4* dst = out + (size_t)r * nch;
+#pragma unroll
+            for (int u = 0; u < kPermU; ++u) {
+                const int c = c0 + u * 64 + lane;
+                if (c < nch) __builtin_nontemporal_store(v[u], dst + c);
+            }
+        }
+    }
+    if (xs) {
+        for (int j = 0; j < K; ++j) {
+            const int r = rid[j];
+            if (r < 0 || r >= R) continue;
+            for (int i = lane; i < nsc; i += 64) outs[(size_t)r * nsc + i] = xs[(size_t)t * nsc + i];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_scales, void* out,
+                          float* out_scales, hipStream_t s) {
+    const moe_desc& d = h->desc;
+    if (d.T == 0) return hipSuccess;
+    const bool fp8 = d.payload == MOE_FP8E4M3_B128;
+    const int row_bytes = fp8 ? d.H : d.H * 2;
+    const int nch = row_bytes / 16;
+    const int nsc = fp8 ? d.H / 128 : 0;
+    hipLaunchKernelGGL(k_permute, dim3((d.T + 3) / 4), dim3(256), 0, s, (const u32x4*)x, d.T, d.K, nch,
+                       (int)d.out_rows, h->row_id, (u32x4*)out, fp8 ? x_scales : nullptr, fp8 ? out_scales : nullptr, nsc);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,286 @@
+// Routing metadata preprocessing (K1): per-expert counts, capacity, padding,
+// segment offsets, the destination row of every copy and the overflow flag,
+// entirely on the device so the host never waits for the counts.
+//
+// Operation: DeepEP PR #716 "perf: reuse HybridEP routing allgather buffer"
+// (sections "Summary", "Memory impact", "Output and gradient regression",
+// "Full HybridEP reference validation") and NeMo-Automodel PR #3931
+// "perf(moe): sync-free HybridEP dispatch" (sections "What does this PR do ?",
+// "Validation").
+//
+// Three launches, all graph-capturable and free of memsets:
+//  1. k_route_tiles  -- one wavefront per 64-token tile.  Every tile builds a
+//     64-bit membership mask per expert in LDS (bit l = token l of the tile
+//     routes to the expert).  popcount(mask) is the tile's count for that
+//     expert and popcount(mask & lanes_below) is a token's stable rank inside
+//     the tile, so ranks are deterministic without ordered atomics.  It also
+//     writes each slot's expert id (or -1) and probability, and tile flags.
+//  2. k_route_scan   -- one 1024-thread workgroup: per-expert exclusive scan
+//     of tile counts, raw counts, capacity, padding, exclusive scan over
+//     experts, rows needed, flag word.
+//  3. k_route_assign -- final destination row of every slot (or -1), source
+//     token of every row (or -1 for pad/unused rows), permuted probabilities.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <int FMT>
+__global__ __launch_bounds__(64) void k_route_tiles(const void* __restrict__ routing,
+                                                    const float* __restrict__ probs,
+                                                    const int32_t* __restrict__ T_live_ptr, int T,
+                                                    int E, int K, uint64_t* __restrict__ tile_mask,
+                                                    int32_t* __restrict__ tile_err,
+                                                    int32_t* __restrict__ row_id,
+                                                    float* __restrict__ copy_prob) {
+    __shared__ unsigned long long msk[kMaxE];
+    const int lane = threadIdx.x;
+    const int tile = blockIdx.x;
+    const int t = tile * kTileTok + lane;
+    int T_live = T;
+    if (T_live_ptr) T_live = min(max(*T_live_ptr, 0), T);
+    for (int e = lane; e < E; e += 64) msk[e] = 0ull;
+    __syncthreads();
+    int err = 0;
+    const bool in = t < T;
+    const bool live = t < T_live;
+    if (FMT != MOE_ROUTE_SPARSE_BOOL) {
+        if (in) {
+            const unsigned long long bit = 1ull << lane;
+            for (int j = 0; j < K; ++j) {
+                const size_t at = (size_t)t * K + j;
+                const int e = (FMT == MOE_ROUTE_DENSE_I16) ? (int)((const int16_t*)routing)[at]
+                                                           : ((const int32_t*)routing)[at];
+                int oute = -1;
+                float p = 0.f;
+                if (live && e != -1) {
+                    if (e < -1 || e >= E) {
+                        err |= MOE_FLAG_BAD_EXPERT;
+                    } else {
+                        // Only this lane touches bit `lane`, and it walks its
+                        // slots in order: the old value says whether the
+                        // expert already occurred earlier in the row.
+                        const unsigned long long old = atomicOr(&msk[e], bit);
+                        if (old & bit) {
+                            err |= MOE_FLAG_DUPLICATE;
+                        } else {
+                            oute = e;
+                            p = probs ? probs[at] : 1.f;
+                        }
+                    }
+                }
+                row_id[at] = oute;
+                copy_prob[at] = p;
+            }
+        }
+    } else {
+        // Boolean map: walk experts in ascending order (wave-uniform loop);
+        // the j-th routed expert of a row fills slot j.
+        int j = 0;
+        const uint8_t* row = (const uint8_t*)routing + (size_t)(live ? t : 0) * E;
+        const bool vec = (E % 16) == 0;
+        for (int e0 = 0; e0 < E; e0 += 16) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (live) {
+                if (vec) {
+                    v = *(const u32x4*)(row + e0);
+                } else {
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+                    for (int i = 0; i < 16 && e0 + i < E; ++i) w[i >> 2] |= (uint32_t)(row[e0 + i] != 0) << ((i & 3) * 8);
+                    v = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int e = e0 + i;
+                const bool r = e < E && ((v[i >> 2] >> ((i & 3) * 8)) & 0xffu) != 0u;
+                bool sel = false;
+                if (r) {
+                    if (j < K) {
+                        const size_t at = (size_t)t * K + j;
+                        row_id[at] = e;
+                        copy_prob[at] = probs ? probs[(size_t)t * E + e] : 1.f;
+                        ++j;
+                        sel = true;
+                    } else {
+                        err |= MOE_FLAG_DUPLICATE;
+                    }
+                }
+                const unsigned long long b = __ballot(sel);
+                if (lane == 0 && e < E) msk[e] = b;
+            }
+        }
+        if (in) {
+            for (; j < K; ++j) {
+                const size_t at = (size_t)t * K + j;
+                row_id[at] = -1;
+                copy_prob[at] = 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    for (int e = lane; e < E; e += 64) tile_mask[(size_t)tile * E + e] = msk[e];
+    const unsigned long long bad = __ballot((err & MOE_FLAG_BAD_EXPERT) != 0);
+    const unsigned long long dup = __ballot((err & MOE_FLAG_DUPLICATE) != 0);
+    if (lane == 0) tile_err[tile] = (bad ? MOE_FLAG_BAD_EXPERT : 0) | (dup ? MOE_FLAG_DUPLICATE : 0);
+}
+
+__global__ __launch_bounds__(1024) void k_route_scan(
+    const uint64_t* __restrict__ tile_mask, const int32_t* __restrict__ tile_err, int n_tiles, int E,
+    int pad, int cap, long long R, int32_t* __restrict__ tile_base, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ kept_out, int64_t* __restrict__ seg_off, int64_t* __restrict__ rows_needed,
+    int32_t* __restrict__ flag) {
+    __shared__ int part[1024];
+    __shared__ long long scan[1024];
+    __shared__ int sflag;
+    const int tid = threadIdx.x;
+    int S = 1;
+    while (S * 2 * E <= 1024) S *= 2;          // S groups of tiles, S*E <= 1024 threads
+    const int chunk = (n_tiles + S - 1) / S;
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+    int terr = 0;
+    for (int i = tid; i < n_tiles; i += 1024) terr |= tile_err[i];
+    if (terr) atomicOr(&sflag, terr);
+
+    const int g = tid / E, e = tid - g * E;
+    const bool act = tid < S * E;
+    const int t0 = g * chunk, t1 = min(n_tiles, t0 + chunk);
+    int sum = 0;
+    if (act) {
+        for (int tl = t0; tl < t1; ++tl) sum += __popcll(tile_mask[(size_t)tl * E + e]);
+        part[g * E + e] = sum;
+    }
+    __syncthreads();
+    if (act) {
+        int run = 0;
+        for (int g2 = 0; g2 < g; ++g2) run += part[g2 * E + e];
+        for (int tl = t0; tl < t1; ++tl) {
+            tile_base[(size_t)tl * E + e] = run;
+            run += __popcll(tile_mask[(size_t)tl * E + e]);
+        }
+    }
+    long long padded = 0;
+    if (tid < E) {
+        int cnt = 0;
+        for (int g2 = 0; g2 < S; ++g2) cnt += part[g2 * E + tid];
+        int kept = cnt;
+        if (cap >= 0 && cnt > cap) {
+            kept = cap;
+            atomicOr(&sflag, MOE_FLAG_CAPACITY);
+        }
+        counts_out[tid] = cnt;
+        kept_out[tid] = kept;
+        padded = ((long long)kept + pad - 1) / pad * pad;
+    }
+    scan[tid] = padded;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const long long v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) seg_off[tid] = scan[tid] - padded;
+    if (tid == E - 1) {
+        seg_off[E] = scan[tid];
+        *rows_needed = scan[tid];
+        if (scan[tid] > R) atomicOr(&sflag, MOE_FLAG_OUT_ROWS);
+    }
+    __syncthreads();
+    if (tid == 0) *flag = sflag;
+}
+
+__global__ __launch_bounds__(256) void k_route_assign(
+    int n_tile_blocks, int n_fill_blocks, int n_tiles, int T, int E, int K, long long R,
+    const uint64_t* __restrict__ tile_mask, const int32_t* __restrict__ tile_base,
+    const int32_t* __restrict__ kept, const int64_t* __restrict__ seg_off,
+    int32_t* __restrict__ row_id, float* __restrict__ copy_prob, int32_t* __restrict__ src_row,
+    float* __restrict__ out_probs) {
+    if ((int)blockIdx.x < n_tile_blocks) {
+        const int lane = threadIdx.x & 63;
+        const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+        if (tile >= n_tiles) return;
+        const int t = tile * kTileTok + lane;
+        if (t >= T) return;
+        const unsigned long long below = (1ull << lane) - 1ull;
+        for (int j = 0; j < K; ++j) {
+            const size_t at = (size_t)t * K + j;
+            const int e = row_id[at];
+            if (e < 0) continue;
+            const size_t te = (size_t)tile * E + e;
+            const int rank = tile_base[te] + __popcll(tile_mask[te] & below);
+            const long long row = seg_off[e] + rank;
+            if (rank < kept[e] && row < R) {
+                row_id[at] = (int)row;
+                src_row[row] = t;
+                if (out_probs) out_probs[row] = copy_prob[at];
+            } else {
+                row_id[at] = -1;
+                copy_prob[at] = 0.f;
+            }
+        }
+        return;
+    }
+    // Rows that hold no copy: padding inside segments, and everything past
+    // the last segment.
+    __shared__ long long s_off[kMaxE + 1];
+    __shared__ int s_kept[kMaxE];
+    for (int i = threadIdx.x; i <= E; i += 256) s_off[i] = seg_off[i];
+    for (int i = threadIdx.x; i < E; i += 256) s_kept[i] = kept[i];
+    __syncthreads();
+    const long long stride = (long long)n_fill_blocks * 256;
+    for (long long r = (long long)(blockIdx.x - n_tile_blocks) * 256 + threadIdx.x; r < R; r += stride) {
+        bool assigned = false;
+        if (r < s_off[E]) {
+            int lo = 0, hi = E - 1;              // last e with s_off[e] <= r
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            assigned = r < s_off[lo] + s_kept[lo];
+        }
+        if (!assigned) {
+            src_row[r] = -1;
+            if (out_probs) out_probs[r] = 0.f;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route(const moe_handle* h, const void* routing, const float* probs,
+                        const int32_t* T_live, int32_t* tokens_per_expert, float* out_probs,
+                        int32_t* flag, hipStream_t s) {
+    const moe_desc& d = h->desc;
+    const int nt = h->n_tiles;
+    if (nt > 0) {
+        switch (d.route_fmt) {
+            case MOE_ROUTE_DENSE_I16:
+                hipLaunchKernelGGL(k_route_tiles<MOE_ROUTE_DENSE_I16>, dim3(nt), dim3(64), 0, s, routing, probs,
+                                   T_live, d.T, d.E, d.K, h->tile_mask, h->tile_err, h->row_id, h->copy_prob);
+                break;
+            case MOE_ROUTE_DENSE_I32:
+                hipLaunchKernelGGL(k_route_tiles<MOE_ROUTE_DENSE_I32>, dim3(nt), dim3(64), 0, s, routing, probs,
+                                   T_live, d.T, d.E, d.K, h->tile_mask, h->tile_err, h->row_id, h->copy_prob);
+                break;
+            default:
+                hipLaunchKernelGGL(k_route_tiles<MOE_ROUTE_SPARSE_BOOL>, dim3(nt), dim3(64), 0, s, routing, probs,
+                                   T_live, d.T, d.E, d.K, h->tile_mask, h->tile_err, h->row_id, h->copy_prob);
+                break;
+        }
+    }
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, h->tile_mask, h->tile_err, nt, d.E,
+                       d.pad_multiple, d.capacity, (long long)d.out_rows, h->tile_base, tokens_per_expert,
+                       h->kept, h->seg_off, h->rows_needed, flag);
+    const int n_tile_blocks = (nt + 3) / 4;
+    long long fb = (d.out_rows + 255) / 256;
+    const int n_fill_blocks = (int)(fb < 1024 ? fb : 1024);
+    if (n_tile_blocks + n_fill_blocks > 0)
+        hipLaunchKernelGGL(k_route_assign, dim3(n_tile_blocks + n_fill_blocks), dim3(256), 0, s, n_tile_blocks,
+                           n_fill_blocks, nt, d.T, d.E, d.K, (long long)d.out_rows, h->tile_mask, h->tile_base,
+                           h->kept, h->seg_off, h->row_id, h->copy_prob, h->src_row, out_probs);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,234 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE layer hot path:
+ *   routing metadata preprocessing -> dispatch-permute -> grouped SwiGLU MLP
+ *   -> probability-weighted combine-unpermute, all experts on one GPU.
+ *
+ * Operations follow these pages (cited by title and section):
+ *   [P1] Megatron-LM PR #6800 "Reuse caller-owned HybridEP dispatch and expert
+ *        output buffers"
+ *   [P2] DeepEP PR #716 "perf: reuse HybridEP routing allgather buffer"
+ *   [P3] NeMo-Automodel PR #3931 "perf(moe): sync-free HybridEP dispatch
+ *        (capacity mode, equal token counts)"
+ *   [P4] Megatron-LM PR #4632 "moe: add DeepEP V2 ElasticBuffer support to MoE
+ *        flex dispatcher"
+ *   [P5] TensorRT-LLM PR #16190 "Update CuTeDSL MegaMoE kernels"
+ *
+ * Conventions for every call below:
+ *   - Pointers prefixed d_ are device memory owned by the caller; the library
+ *     never allocates, frees or keeps them beyond the call (the workspace is
+ *     only referenced through the handle until it is re-initialised).
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Device work is enqueued on it asynchronously; no call synchronises the
+ *     host with the device, so every sequence is capturable in a HIP graph.
+ *   - Shapes are fixed when a handle is initialised (static-shape rule of
+ *     [P4] "What changed": the per-rank token ceiling is pinned at
+ *     construction).  Host-side argument checks return a negative status and
+ *     enqueue nothing; device-side problems are reported only through the
+ *     overflow flag word.
+ *   - bf16 tensors are raw 16-bit patterns; fp8 is OCP e4m3 ("fn") with one
+ *     fp32 scale per 128 consecutive columns of a row.
+ *   - Device pointers to token rows must be 16-byte aligned.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* ---- status codes --------------------------------------------------------- */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* null required pointer, unknown enum value      */
+    MOE_ESHAPE = -2,        /* sizes outside the supported ranges             */
+    MOE_EDTYPE = -3,        /* dtype / format combination not supported       */
+    MOE_EALIGN = -4,        /* a device pointer is not 16-byte aligned         */
+    MOE_ESTALE = -5,        /* handle's workspace was re-initialised, or the   */
+                            /* handle has no routing metadata yet             */
+    MOE_EHIP = -6,          /* a HIP runtime call failed                       */
+    MOE_EUNSUPPORTED = -7,  /* legal but not implemented                       */
+    MOE_ENOSPC = -8         /* workspace or scratch smaller than required      */
+};
+
+/* ---- routing formats ([P2] "Memory impact", "Implementation") -------------
+ * DENSE_*: top-k expert indices [T, K], -1 marks an empty slot.
+ * SPARSE_BOOL: Boolean map [T, E], one byte per (token, expert), nonzero =
+ * routed; K then bounds the experts per token. */
+enum moe_route_fmt {
+    MOE_ROUTE_DENSE_I16 = 0,
+    MOE_ROUTE_DENSE_I32 = 1,
+    MOE_ROUTE_SPARSE_BOOL = 2
+};
+
+/* ---- payload / weight dtypes ([P2] "Full HybridEP reference validation":
+ * BF16 and FP8 dispatch; [P5] first commit message: low-precision weights) */
+enum moe_dtype {
+    MOE_BF16 = 0,
+    MOE_FP8E4M3_B128 = 1    /* e4m3 codes + fp32 scale per 128 columns         */
+};
+
+/* ---- overflow flag bits ([P3] "What does this PR do ?", "Validation": the
+ * real counts stay on the device and an overflow flag reports truncation).
+ * The flag word is written fresh (not accumulated) by every preprocess. */
+#define MOE_FLAG_CAPACITY   1  /* some expert count exceeds the capacity          */
+#define MOE_FLAG_OUT_ROWS   2  /* padded segments need more rows than out_rows    */
+#define MOE_FLAG_BAD_EXPERT 4  /* a dense index outside [-1, E)                   */
+#define MOE_FLAG_DUPLICATE  8  /* repeated expert in a dense row, or more than K  */
+                               /* experts in a sparse row                          */
+
+/* Static description of one dispatch/combine problem. */
+typedef struct moe_desc {
+    int32_t T;             /* tokens (rows of x), >= 0                           */
+    int32_t H;             /* hidden size; bf16: multiple of 8, fp8: of 128      */
+    int32_t E;             /* experts, 1..1024                                   */
+    int32_t K;             /* top-k slots (dense) / max experts per row (sparse) */
+    int32_t route_fmt;     /* enum moe_route_fmt                                 */
+    int32_t payload;       /* enum moe_dtype of the permuted rows                */
+    int32_t pad_multiple;  /* >= 1; each expert segment is padded to a multiple  */
+    int32_t capacity;      /* rows kept per expert; < 0 = unbounded              */
+    int64_t out_rows;      /* rows R of the permuted / expert-output buffers;    */
+                           /* 0 = moe_out_rows_bound(desc)                        */
+} moe_desc;
+
+/* Dispatch handle: plain data.  Host ints plus device pointers carved from
+ * the caller's workspace; it owns nothing.  Fields are read-only for the
+ * caller.  Device arrays (all in the workspace):
+ *   seg_off[E+1]  int64  first row of each expert segment (exclusive scan of
+ *                        the padded kept counts); seg_off[E] = rows needed
+ *   kept[E]       int32  copies kept per expert (min(count, capacity))
+ *   row_id[T*K]   int32  destination row of copy (t, j), -1 if none
+ *   copy_prob[T*K] f32   probability of copy (t, j) (1 without probs, 0 if
+ *                        dropped)
+ *   src_row[R]    int32  source token of each row, -1 for rows with no copy */
+typedef struct moe_handle {
+    moe_desc desc;         /* resolved copy (out_rows filled in)                 */
+    uint64_t epoch;        /* workspace generation                               */
+    int32_t n_tiles;       /* 64-token tiles                                      */
+    int32_t state;         /* 0 = initialised, 1 = routing metadata enqueued     */
+    void* ws;
+    size_t ws_bytes;
+    uint64_t* tile_mask;   /* [n_tiles, E] per-tile expert membership bitmasks    */
+    int32_t* tile_base;    /* [n_tiles, E] copies of each expert in earlier tiles */
+    int32_t* tile_err;     /* [n_tiles] per-tile flag bits                        */
+    int64_t* seg_off;
+    int32_t* kept;
+    int64_t* rows_needed;  /* [1]                                                 */
+    int32_t* row_id;
+    float* copy_prob;
+    int32_t* src_row;
+} moe_handle;
+
+/* ---- host-only helpers (no device access) ---------------------------------- */
+
+/* Text for a status code. */
+const char* moe_status_string(int status);
+
+/* Largest number of rows the padded segments can need:
+ * min(E * roundup(capacity, p), T*K + E*(p-1)); the second term alone when
+ * capacity < 0.  Returns -1 for an invalid descriptor. */
+int64_t moe_out_rows_bound(const moe_desc* desc);
+
+/* Bytes of one routing tensor of this descriptor: T*E for the Boolean map,
+ * T*K*2 (int16) or T*K*4 (int32) for dense indices.  [P2] "Memory impact". */
+int64_t moe_routing_bytes(const moe_desc* desc);
+
+/* Caller-side static bound from a calibrated row count: ceil(rows * factor)
+ * rounded up to a multiple of 4.  [P3] "What does this PR do ?" and the
+ * calibration figure under "Validation".  Returns -1 if rows < 0 or
+ * factor <= 0. */
+int64_t moe_capacity_from_rows(int64_t rows, double factor);
+
+/* Workspace bytes needed by a handle for this descriptor (0 if invalid). */
+size_t moe_workspace_bytes(const moe_desc* desc);
+
+/* Validate `desc`, resolve out_rows, carve the caller's workspace d_ws
+ * (ws_bytes >= moe_workspace_bytes) and fill *h.  Host only: touches no
+ * device memory.  Re-initialising a workspace makes earlier handles on it
+ * stale (later calls with them return MOE_ESTALE), the explicit early-reuse
+ * failure of [P1] "Summary". */
+int moe_handle_init(const moe_desc* desc, void* d_ws, size_t ws_bytes, moe_handle* h);
+
+/* ---- device calls (asynchronous on `stream`) -------------------------------- */
+
+/* Routing metadata preprocessing.  [P2] "Summary" (metadata preprocessing
+ * consumes the routing map on the dispatch stream), [P3] "What does this PR
+ * do ?" (counts and an overflow flag left on the device, no host sync),
+ * [P4] "Motivation" (layout inferred from the top-k indices).
+ *   d_routing            [T,K] int16/int32 or [T,E] uint8 per desc.route_fmt
+ *   d_probs              nullable; fp32 with the routing's shape
+ *   d_T_live             nullable; device int32 count of live tokens, tokens
+ *                        at or beyond it are unrouted (decode bucket trim,
+ *                        [P5] review-fix commit)
+ *   d_tokens_per_expert  [E] int32 out: raw per-expert copy counts
+ *   d_out_probs          nullable [R] fp32 out: probability of each row's copy,
+ *                        0 for rows holding no copy
+ *   d_flag               [1] int32 out: MOE_FLAG_* bits, written fresh
+ * Rows inside an expert segment follow token order; an expert keeps its first
+ * `capacity` copies; copies that would land at or beyond out_rows are
+ * dropped. */
+int moe_route_preprocess(moe_handle* h, const void* d_routing, const float* d_probs,
+                         const int32_t* d_T_live, int32_t* d_tokens_per_expert,
+                         float* d_out_probs, int32_t* d_flag, void* stream);
+
+/* Permute: copy every kept token row to its destination row.  [P1]
+ * "Summary"/"Configuration" (dispatch writes permuted tokens into a
+ * caller-provided output buffer), [P2] "Full HybridEP reference validation"
+ * (dispatch with permutation, BF16 and FP8).
+ *   d_x         [T,H] bf16, or [T,H] e4m3 codes for desc.payload = FP8
+ *   d_x_scales  fp8 only: [T, H/128] fp32; else NULL
+ *   d_out       [R,H] same dtype as d_x; rows without a copy are not written
+ *   d_out_scales fp8 only: [R, H/128] fp32 */
+int moe_permute(const moe_handle* h, const void* d_x, const float* d_x_scales, void* d_out,
+                float* d_out_scales, void* stream);
+
+/* moe_route_preprocess followed by moe_permute on the same stream. */
+int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs,
+                 const int32_t* d_T_live, const void* d_x, const float* d_x_scales, void* d_out,
+                 float* d_out_scales, float* d_out_probs, int32_t* d_tokens_per_expert,
+                 int32_t* d_flag, void* stream);
+
+/* Scratch bytes moe_grouped_swiglu_mlp needs for FFN width F and weight
+ * dtype wdtype (the FC1 activations of all R rows). 0 if invalid. */
+size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype);
+
+/* Grouped expert MLP over the permuted rows: for every expert e and every
+ * kept row r of its segment, g = W1[e][0:F] x_r, u = W1[e][F:2F] x_r,
+ * a = silu(g) * u, y_r = W2[e] a, y_r stored as bf16 into the caller-owned
+ * d_expert_out.  [P1] "Summary" and "Configuration" (grouped MLP writing FC2
+ * into a caller-provided reusable buffer), [P5] streaming-load commit (FC1
+ * weight is the concatenated gate/up matrix).
+ *   d_perm        [R,H] bf16 permuted rows (output of moe_permute)
+ *   d_perm_scales reserved, must be NULL
+ *   wdtype MOE_BF16: d_w1 [E,2F,H] bf16, d_w2 [E,H,F] bf16, scales NULL;
+ *          requires H % 256 == 0 and F % 128 == 0.
+ *   wdtype MOE_FP8E4M3_B128: d_w1 [E,2F,H] e4m3, d_w1_scales [E,2F/128,H/128]
+ *          fp32, d_w2 [E,H,F] e4m3, d_w2_scales [E,H/128,F/128] fp32; the
+ *          bf16 rows are quantised per 1x128 block on load and a is
+ *          re-quantised per 1x128 block; requires H, F multiples of 128.
+ *   d_scratch     >= moe_mlp_scratch_bytes bytes
+ *   d_expert_out  [R,H] bf16; rows that hold no kept copy are unspecified */
+int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
+                           const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
+                           const void* d_w2, const float* d_w2_scales, void* d_scratch,
+                           size_t scratch_bytes, void* d_expert_out, void* stream);
+
+/* Combine-unpermute: y[t] = bf16( sum over the token's surviving copies j, in
+ * slot order, of p_tj * expert_out[row_id[t,j]] ) accumulated in fp32;
+ * p_tj = copy probability if apply_probs else 1; a token with no surviving
+ * copy gets 0.  [P1] "Summary"/"Motivation" (combine is the final read of the
+ * expert output), [P5] review-fix commit (top-k reduction).
+ *   d_expert_out  [R,H] bf16
+ *   d_y           [T,H] bf16 out */
+int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_probs, void* d_y,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

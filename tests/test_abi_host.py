@@ -1,0 +1,173 @@
+"""The C-ABI library loads, exports every symbol include/moe_route.h
+declares, and its host-only logic (validation, sizing, workspace carving,
+stale-handle detection, page-pinned helpers) behaves as documented.  No call
+here reaches the GPU: every device call below is rejected by host checks."""
+import ctypes as C
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from combine_routing_preprocess_amd import _abi as A
+from combine_routing_preprocess_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "page_values.json")))
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 12, names
+    L = A.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(n for n, _, _ in A.SIGNATURES) == names
+
+
+def _desc(**kw):
+    base = dict(T=100, H=256, E=8, K=2, route_fmt="dense_i16", payload="bf16", pad_multiple=4, capacity=None,
+                out_rows=0)
+    base.update(kw)
+    return api.make_desc(**base)
+
+
+def test_status_strings():
+    for s in range(-8, 1):
+        assert A.status_string(s)
+
+
+def test_out_rows_bound_is_safe_and_reached():
+    L = A.lib()
+    r = np.random.default_rng(0)
+    for _ in range(100):
+        T, E = int(r.integers(0, 50)), int(r.integers(1, 9))
+        K, pad, cap = int(r.integers(1, E + 1)), int(r.integers(1, 6)), int(r.integers(-1, 10))
+        d = api.make_desc(T, 64, E, K, pad_multiple=pad, capacity=None if cap < 0 else cap)
+        bound = L.moe_out_rows_bound(C.byref(d))
+        idx = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int16)
+        rt = oracle.route(idx, 0, E, K, pad=pad, cap=cap, R=10 ** 6)
+        assert rt["rows_needed"] <= bound
+    # reached: one token per expert with a large padding multiple, no capacity
+    d = api.make_desc(4, 64, 4, 1, pad_multiple=8)
+    assert L.moe_out_rows_bound(C.byref(d)) == 4 + 4 * 7
+    rt = oracle.route(np.arange(4, dtype=np.int16).reshape(4, 1), 0, 4, 1, pad=8, R=100)
+    assert rt["rows_needed"] == 32
+    # reached through the capacity term: every expert full
+    d = api.make_desc(8, 64, 2, 2, pad_multiple=3, capacity=4)
+    assert L.moe_out_rows_bound(C.byref(d)) == 2 * 6
+
+
+def test_page_value_helpers():
+    g = GOLD["routing_bytes"]
+    tok = g["tokens_per_rank"] * g["world_size"]
+    assert api.routing_bytes(tok, g["experts"], g["topk"], "sparse_bool") == g["sparse_bool_bytes_per_rank"]
+    assert api.routing_bytes(tok, g["experts"], g["topk"], "dense_i16") == g["dense_int16_bytes_per_rank"]
+    c = GOLD["capacity_calibration"]
+    assert api.capacity_from_rows(c["rows"], c["factor"]) == c["capacity"]
+    assert api.capacity_from_rows(10, 1.5) == 16
+    assert api.capacity_from_rows(-1, 1.5) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=0), A.MOE_ESHAPE), (dict(E=1025), A.MOE_ESHAPE), (dict(K=0), A.MOE_ESHAPE),
+    (dict(T=-1), A.MOE_ESHAPE), (dict(pad_multiple=0), A.MOE_ESHAPE), (dict(H=12), A.MOE_ESHAPE),
+    (dict(payload="fp8", H=192), A.MOE_ESHAPE), (dict(out_rows=-5), A.MOE_ESHAPE),
+    (dict(out_rows=2 ** 31), A.MOE_ESHAPE),
+])
+def test_invalid_descriptors_are_rejected(kw, status):
+    d = _desc(**kw)
+    L = A.lib()
+    assert L.moe_workspace_bytes(C.byref(d)) == 0
+    buf = (C.c_uint8 * 4096)()
+    h = A.MoeHandle()
+    assert L.moe_handle_init(C.byref(d), C.cast(buf, C.c_void_p), 4096, C.byref(h)) == status
+
+
+def test_bad_enum_and_null():
+    L = A.lib()
+    d = _desc()
+    d.route_fmt = 7
+    h = A.MoeHandle()
+    assert L.moe_handle_init(C.byref(d), C.c_void_p(256), 1 << 20, C.byref(h)) == A.MOE_EINVAL
+    d = _desc()
+    d.payload = 9
+    assert L.moe_handle_init(C.byref(d), C.c_void_p(256), 1 << 20, C.byref(h)) == A.MOE_EDTYPE
+    d = _desc()
+    assert L.moe_handle_init(C.byref(d), None, 1 << 20, C.byref(h)) == A.MOE_EINVAL
+    assert L.moe_handle_init(C.byref(d), C.c_void_p(264), 1 << 20, C.byref(h)) == A.MOE_EALIGN
+
+
+def _host_handle(desc, extra=0):
+    """Initialise a handle over a host buffer: moe_handle_init only carves
+    addresses, it never dereferences the workspace."""
+    L = A.lib()
+    n = L.moe_workspace_bytes(C.byref(desc))
+    buf = (C.c_uint8 * (n + 256 + extra))()
+    base = (C.addressof(buf) + 255) // 256 * 256
+    h = A.MoeHandle()
+    rc = L.moe_handle_init(C.byref(desc), C.c_void_p(base), n, C.byref(h))
+    return rc, h, base, n, buf
+
+
+def test_workspace_carving():
+    d = _desc(T=1000, E=32, K=8, pad_multiple=16, capacity=300)
+    rc, h, base, n, _buf = _host_handle(d)
+    assert rc == 0
+    R = h.desc.out_rows
+    assert R == min(32 * 304, 1000 * 8 + 32 * 15)
+    assert h.n_tiles == (1000 + 63) // 64
+    fields = [("tile_mask", h.n_tiles * 32 * 8), ("tile_base", h.n_tiles * 32 * 4), ("tile_err", h.n_tiles * 4),
+              ("seg_off", 33 * 8), ("kept", 32 * 4), ("rows_needed", 8), ("row_id", 8000 * 4),
+              ("copy_prob", 8000 * 4), ("src_row", R * 4)]
+    spans = sorted((getattr(h, f) - base, sz) for f, sz in fields)
+    for (o1, s1), (o2, _) in zip(spans, spans[1:]):
+        assert o1 + s1 <= o2                      # no overlap
+    assert all(o % 256 == 0 for o, _ in spans)
+    assert spans[-1][0] + spans[-1][1] <= n
+    # too small a workspace
+    L = A.lib()
+    h2 = A.MoeHandle()
+    assert L.moe_handle_init(C.byref(d), C.c_void_p(base), n - 1, C.byref(h2)) == A.MOE_ENOSPC
+
+
+def test_stale_handle_and_missing_routing_are_rejected_before_launch():
+    L = A.lib()
+    d = _desc()
+    rc, h1, base, n, _buf = _host_handle(d)
+    assert rc == 0
+    # no routing metadata yet: permute / MLP / combine refuse
+    x = C.c_void_p(base)
+    assert L.moe_permute(C.byref(h1), x, None, x, None, None) == A.MOE_ESTALE
+    assert L.moe_combine(C.byref(h1), x, 1, x, None) == A.MOE_ESTALE
+    assert L.moe_grouped_swiglu_mlp(C.byref(h1), 128, 0, x, None, x, None, x, None, x, 1 << 30, x, None) == A.MOE_ESTALE
+    # re-initialising the workspace makes the first handle stale
+    h2 = A.MoeHandle()
+    assert L.moe_handle_init(C.byref(d), C.c_void_p(base), n, C.byref(h2)) == 0
+    assert h2.epoch == h1.epoch + 1
+    assert L.moe_route_preprocess(C.byref(h1), x, None, None, x, None, x, None) == A.MOE_ESTALE
+    # null required pointers
+    assert L.moe_route_preprocess(C.byref(h2), None, None, None, x, None, x, None) == A.MOE_EINVAL
+    assert L.moe_route_preprocess(C.byref(h2), x, None, None, None, None, x, None) == A.MOE_EINVAL
+    # misaligned routing
+    assert L.moe_route_preprocess(C.byref(h2), C.c_void_p(base + 2), None, None, x, None, x, None) == A.MOE_EALIGN
+
+
+def test_scratch_sizing():
+    d = _desc(T=64, E=4, K=2, pad_multiple=1)
+    rc, h, base, n, _buf = _host_handle(d)
+    L = A.lib()
+    R = h.desc.out_rows
+    assert L.moe_mlp_scratch_bytes(C.byref(h), 256, A.BF16) >= R * 256 * 2
+    assert L.moe_mlp_scratch_bytes(C.byref(h), 256, A.FP8E4M3_B128) >= R * 256 + R * 2 * 4
+    assert L.moe_mlp_scratch_bytes(C.byref(h), 100, A.FP8E4M3_B128) == 0
+    assert L.moe_mlp_scratch_bytes(C.byref(h), 0, A.BF16) == 0
