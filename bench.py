@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+One step = routing metadata preprocessing -> permute -> grouped FC1 + SwiGLU
+-> grouped FC2 (into a reused caller-owned buffer) -> combine, over one batch
+of the DeepSeek-V3-shaped synthetic workload: 8192 tokens x 7168 bf16, 256
+experts top-8 (sigmoid scores, renormalised), FFN 2048, padding multiple 128.
+Inputs and weights are resident in HBM before timing starts.
+
+Prints one JSON line (stdout).  Per-stage times come from HIP events recorded
+on the stream the kernels run on; the roofline entry is for the dominant
+kernel (grouped FC1 + SwiGLU).  The CPU baseline times the plain oracle on a
+small token sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+METRIC = "permute+combine HBM GB/s (% peak); MoE-layer tokens/s at 8192x7168, 256E top-8"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fc1_dsv3_layer.json")
+FC1_SOURCE = os.path.join(ROOT, "combine_routing_preprocess_amd", "csrc", "gemm_bf16.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_units: dict):
+    """HBM bytes per FC1 launch from committed rocprofv3 counter summaries, or
+    None when they are missing or were taken on a different kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != source_hash(FC1_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="oracle sample size (0 = skip)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU layer: every expert is local to one MI355X and there is no "
+              "cross-GPU exchange in this build, so --gpus must be 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import moe_synth as S
+    from combine_routing_preprocess_amd import Dispatcher
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda"
+    c = S.CONFIGS["cfg4_dsv3_layer"]
+    T, H, E, K, F, pad = c.T, c.H, c.E, c.K, c.F, c.pad
+
+    # ---- inputs, resident in HBM -------------------------------------------
+    idx, pr = S.route_sigmoid_topk(T, E, K, c.seed)
+    x_np = S.bf16_normal((T, H), c.seed)
+    x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    routing = torch.from_numpy(idx).to(dev)
+    probs = torch.from_numpy(pr).to(dev)
+    log("drawing weights on the device")
+    w1 = S.weights_bf16(E, 2 * F, H, c.seed + 1, device=dev)
+    w2 = S.weights_bf16(E, H, F, c.seed + 2, device=dev)
+    d = Dispatcher(T, H, E, K, pad_multiple=pad)
+    perm = torch.empty((d.R, H), dtype=torch.bfloat16, device=dev)
+    scratch = d.alloc_mlp_scratch(F)
+    expert_out = torch.empty((d.R, H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        d.preprocess(routing, probs)
+        if ev is not None:
+            ev[1].record()
+        d.permute(x, out=perm)
+        if ev is not None:
+            ev[2].record()
+        d.fc1(perm, w1, scratch)
+        if ev is not None:
+            ev[3].record()
+        d.fc2(w2, scratch, expert_out)
+        if ev is not None:
+            ev[4].record()
+        d.combine(expert_out, out=y)
+        if ev is not None:
+            ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(d.flag.item()) == 0, "routing flag set"
+    kept = d.kept.cpu().numpy().astype(np.int64)
+    n_copies = int(kept.sum())
+    touched = int((kept > 0).sum())
+
+    # ---- timed region ------------------------------------------------------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_s = T * args.steps / (t1 - t0)
+
+    names = ["preprocess", "permute", "fc1_swiglu", "fc2", "combine"]
+    stage_ms = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)] for j, n in enumerate(names)}
+    mean = {n: statistics.fmean(v) for n, v in stage_ms.items()}
+    mins = {n: min(v) for n, v in stage_ms.items()}
+
+    # ---- algorithmic work per launch (kept copies only, no padding rows) ------
+    b = 2  # bf16 bytes
+    work = {
+        "permute": dict(bytes=T * H * b + n_copies * H * b),
+        "combine": dict(bytes=n_copies * H * b + T * H * b),
+        "fc1_swiglu": dict(bytes=touched * 2 * F * H * b + n_copies * H * b + n_copies * F * b,
+                           flops=2 * n_copies * H * 2 * F),
+        "fc2": dict(bytes=touched * H * F * b + n_copies * F * b + n_copies * H * b, flops=2 * n_copies * F * H),
+    }
+    stages = {}
+    for n in names:
+        s = {"mean_ms": round(mean[n], 4), "min_ms": round(mins[n], 4)}
+        if n in work:
+            s["alg_bytes"] = work[n]["bytes"]
+            s["GB_s"] = round(work[n]["bytes"] / (mean[n] * 1e-3) / 1e9, 1)
+            s["hbm_frac"] = round(s["GB_s"] / HBM_PEAK_GBS, 4)
+            if "flops" in work[n]:
+                s["alg_flops"] = work[n]["flops"]
+                s["TFLOP_s"] = round(work[n]["flops"] / (mean[n] * 1e-3) / 1e12, 1)
+                s["mfma_frac"] = round(s["TFLOP_s"] / BF16_PEAK_TFLOPS, 4)
+        stages[n] = s
+
+    fc1 = work["fc1_swiglu"]
+    t_fc1 = mean["fc1_swiglu"] * 1e-3
+    hbm_time = fc1["bytes"] / (HBM_PEAK_GBS * 1e9)
+    mfma_time = fc1["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    if hbm_time >= mfma_time:
+        roof = {"bound": "hbm", "achieved": round(fc1["bytes"] / t_fc1 / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(fc1["flops"] / t_fc1 / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(fc1)
+    roof["kernel"] = "k_gemm_bf16<0> (grouped FC1 + SwiGLU)"
+    roof["alg_bytes_per_launch"] = fc1["bytes"]
+    roof["alg_flops_per_launch"] = fc1["flops"]
+    roof["mfma_frac"] = stages["fc1_swiglu"]["mfma_frac"]
+
+    pc_bytes = work["permute"]["bytes"] + work["combine"]["bytes"]
+    pc_ms = mean["permute"] + mean["combine"]
+    permute_combine = {"GB_s": round(pc_bytes / (pc_ms * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(pc_bytes / (pc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "permute_GB_s": stages["permute"]["GB_s"], "combine_GB_s": stages["combine"]["GB_s"]}
+
+    # ---- HIP-graph replay of the whole step ------------------------------------
+    graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(20):
+            a, bq = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            bq.record()
+            bq.synchronize()
+            reps.append(a.elapsed_time(bq))
+        graph = {"min_ms": round(min(reps), 4), "median_ms": round(statistics.median(reps), 4),
+                 "tokens_per_s_at_min": round(T / (min(reps) * 1e-3), 1)}
+
+    # ---- CPU baseline: the oracle on a token sample of the same batch ----------
+    cpu = None
+    if args.cpu_tokens > 0:
+        import oracle
+        n = min(args.cpu_tokens, T)
+        toks = np.arange(n)
+        rt0 = oracle.route(idx, oracle.FMT_DENSE_I16, E, K, pr, pad)
+        need = sorted({int(e) for e in rt0["copy_expert"][:n].reshape(-1) if e >= 0})
+        log(f"copying {len(need)} experts' weights to the host for the oracle sample")
+        w1h = {e: w1[e].view(torch.int16).cpu().numpy().view(np.uint16) for e in need}
+        w2h = {e: w2[e].view(torch.int16).cpu().numpy().view(np.uint16) for e in need}
+        tc0 = time.perf_counter()
+        rt = oracle.route(idx, oracle.FMT_DENSE_I16, E, K, pr, pad)
+        yo = oracle.layer_tokens(toks, x_np, rt, lambda e, rows: oracle.expert_mlp_bf16(rows, w1h[e], w2h[e]))
+        tc1 = time.perf_counter()
+        got = y[:n].view(torch.int16).cpu().numpy().view(np.uint16)
+        gf, of = S.bf16_to_float(got).astype(np.float64), S.bf16_to_float(yo).astype(np.float64)
+        rel = float(np.linalg.norm(gf - of) / np.linalg.norm(of))
+        cpu = {"value": round(n / (tc1 - tc0), 4), "unit": "tokens/s", "cores": oracle.get_threads(),
+               "kind": "oracle",
+               "sample": f"first {n} of {T} tokens: routing metadata for the whole batch, then each sampled "
+                         f"token's {K} expert MLPs (fp64 loops) and its combine; {tc1 - tc0:.1f} s",
+               "seconds": round(tc1 - tc0, 2), "gpu_vs_oracle_rel_l2": rel}
+        del w1h, w2h
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dsv3_layer: 8192 tokens x 7168 bf16, 256 experts top-8 (sigmoid, renormalised), "
+                               "SwiGLU FFN 2048, padding multiple 128, dense int16 routing",
+                   "T": T, "H": H, "E": E, "K": K, "F": F, "pad_multiple": pad, "out_rows": d.R,
+                   "kept_rows": n_copies, "experts_touched": touched, "parallelism": "1 GPU, all experts local"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "permute_combine": permute_combine,
+        "stages": stages,
+        "graph_replay": graph,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -46,6 +46,9 @@ SIGNATURES = [
     ("moe_mlp_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32, C.c_int32]),
     ("moe_grouped_swiglu_mlp", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P,
                                          _P, C.c_size_t, _P, _P]),
+    ("moe_grouped_fc1_swiglu", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, _P, _P,
+                                         C.c_size_t, _P]),
+    ("moe_grouped_fc2", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P, _P]),
     ("moe_combine", C.c_int, [C.POINTER(MoeHandle), _P, C.c_int32, _P, _P]),
 ]
 

@@ -231,6 +231,24 @@ class Dispatcher:
                                                scratch.numel(), _ptr(out), _stream()), "moe_grouped_swiglu_mlp")
         return out
 
+    def fc1(self, perm: torch.Tensor, w1: torch.Tensor, scratch: torch.Tensor, w1_scales=None) -> None:
+        """FC1 + SwiGLU of every kept row into ``scratch`` (the first half of
+        grouped_mlp)."""
+        F = w1.shape[1] // 2
+        wdtype = "fp8" if w1.dtype in _FP8_DTYPES else "bf16"
+        A.check(A.lib().moe_grouped_fc1_swiglu(C.byref(self.h), F, _DT[wdtype], _ptr(perm), None, _ptr(w1),
+                                               _ptr(w1_scales), _ptr(scratch), scratch.numel(), _stream()),
+                "moe_grouped_fc1_swiglu")
+
+    def fc2(self, w2: torch.Tensor, scratch: torch.Tensor, out: torch.Tensor, w2_scales=None) -> torch.Tensor:
+        """FC2 from ``scratch`` into the caller-owned ``out`` (the second half
+        of grouped_mlp)."""
+        F = w2.shape[2]
+        wdtype = "fp8" if w2.dtype in _FP8_DTYPES else "bf16"
+        A.check(A.lib().moe_grouped_fc2(C.byref(self.h), F, _DT[wdtype], _ptr(w2), _ptr(w2_scales), _ptr(scratch),
+                                        scratch.numel(), _ptr(out), _stream()), "moe_grouped_fc2")
+        return out
+
     def combine(self, expert_out: torch.Tensor, apply_probs: bool = True, out: Optional[torch.Tensor] = None):
         self._dev(expert_out, "expert_out")
         _need(expert_out.dtype == torch.bfloat16 and tuple(expert_out.shape) == (self.R, self.H),

@@ -21,12 +21,13 @@ SOURCES = ["api.cpp", "route.hip", "permute.hip", "combine.hip", "gemm_bf16.hip"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+          "-Wno-inline-asm"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, out_dir: str = OUT_DIR, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + COMMON + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in r.stdout.splitlines() if noise not in l)
@@ -37,17 +38,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = True, lib_path: str = LIB, extra=()) -> str:
+    """Compile every source and link the shared library.  ``extra`` adds
+    compiler flags (e.g. -D overrides of compile-time tile parameters) and
+    ``lib_path`` redirects the output for such variant builds."""
+    out_dir = OUT_DIR if lib_path == LIB else os.path.join(os.path.dirname(lib_path), "_build")
+    os.makedirs(out_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, out_dir, extra), SOURCES))
+    LIBP = lib_path
+    tmp = LIBP + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + ["-Wl,--no-undefined"]
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, LIBP)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {LIBP}")
+    return LIBP
 
 
 if __name__ == "__main__":

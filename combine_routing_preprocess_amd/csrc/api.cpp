@@ -231,30 +231,71 @@ size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype) {
     return 0;
 }
 
-int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
-                           const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
-                           const void* d_w2, const float* d_w2_scales, void* d_scratch,
-                           size_t scratch_bytes, void* d_expert_out, void* stream) {
+namespace {
+
+// Checks shared by the MLP entry points; *ncu receives the CU count.
+int check_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* w, const float* w_scales,
+              const void* scratch, size_t scratch_bytes, int* ncu) {
     int rc = check_handle(h, true);
     if (rc) return rc;
     const moe_desc& d = h->desc;
     if (F <= 0) return MOE_ESHAPE;
-    if (d.payload != MOE_BF16 || d_perm_scales) return MOE_EDTYPE;
-    if (!d_perm || !d_w1 || !d_w2 || !d_expert_out || !d_scratch) return MOE_EINVAL;
-    if (!al16(d_perm) || !al16(d_w1) || !al16(d_w2) || !al16(d_expert_out) || !al16(d_scratch)) return MOE_EALIGN;
+    if (d.payload != MOE_BF16) return MOE_EDTYPE;
+    if (!w || !scratch) return MOE_EINVAL;
+    if (!al16(w) || !al16(scratch)) return MOE_EALIGN;
     const size_t need = moe_mlp_scratch_bytes(h, F, wdtype);
     if (need == 0) return MOE_ESHAPE;
     if (scratch_bytes < need) return MOE_ENOSPC;
-    const int ncu = num_cu();
-    if (ncu <= 0) return MOE_EHIP;
     if (wdtype == MOE_BF16) {
-        if (d_w1_scales || d_w2_scales) return MOE_EDTYPE;
+        if (w_scales) return MOE_EDTYPE;
         if (d.H % 256 || F % 128) return MOE_ESHAPE;
-        return hip_rc(launch_mlp_bf16(h, F, d_perm, d_w1, d_w2, d_scratch, d_expert_out, ncu,
-                                      (hipStream_t)stream));
+    } else if (wdtype == MOE_FP8E4M3_B128) {
+        return MOE_EUNSUPPORTED;
+    } else {
+        return MOE_EDTYPE;
     }
-    if (wdtype == MOE_FP8E4M3_B128) return MOE_EUNSUPPORTED;
-    return MOE_EDTYPE;
+    *ncu = num_cu();
+    return *ncu > 0 ? MOE_OK : MOE_EHIP;
+}
+
+}  // namespace
+
+int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
+                           const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
+                           void* d_scratch, size_t scratch_bytes, void* stream) {
+    int ncu = 0;
+    int rc = check_mlp(h, F, wdtype, d_w1, d_w1_scales, d_scratch, scratch_bytes, &ncu);
+    if (rc) return rc;
+    if (d_perm_scales) return MOE_EDTYPE;
+    if (!d_perm) return MOE_EINVAL;
+    if (!al16(d_perm)) return MOE_EALIGN;
+    return hip_rc(launch_gemm_bf16(h, 0, F, d_perm, d_w1, d_scratch, ncu, (hipStream_t)stream));
+}
+
+int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_w2,
+                    const float* d_w2_scales, const void* d_scratch, size_t scratch_bytes,
+                    void* d_expert_out, void* stream) {
+    int ncu = 0;
+    int rc = check_mlp(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, &ncu);
+    if (rc) return rc;
+    if (!d_expert_out) return MOE_EINVAL;
+    if (!al16(d_expert_out)) return MOE_EALIGN;
+    return hip_rc(launch_gemm_bf16(h, 1, F, d_scratch, d_w2, d_expert_out, ncu, (hipStream_t)stream));
+}
+
+int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
+                           const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
+                           const void* d_w2, const float* d_w2_scales, void* d_scratch,
+                           size_t scratch_bytes, void* d_expert_out, void* stream) {
+    int ncu = 0;
+    int rc = check_mlp(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, &ncu);
+    if (rc) return rc;
+    if (!d_expert_out) return MOE_EINVAL;
+    if (!al16(d_expert_out)) return MOE_EALIGN;
+    rc = moe_grouped_fc1_swiglu(h, F, wdtype, d_perm, d_perm_scales, d_w1, d_w1_scales, d_scratch,
+                                scratch_bytes, stream);
+    if (rc) return rc;
+    return moe_grouped_fc2(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, d_expert_out, stream);
 }
 
 int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_probs, void* d_y,

@@ -31,8 +31,9 @@ hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_sca
                           float* out_scales, hipStream_t s);
 hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs, void* y_out,
                           hipStream_t s);
-hipError_t launch_mlp_bf16(const moe_handle* h, int F, const void* perm, const void* w1,
-                           const void* w2, void* act, void* expert_out, int num_cu, hipStream_t s);
+// stage 0: FC1 + SwiGLU (in -> act), stage 1: FC2 (act -> expert_out)
+hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* in, const void* w,
+                            void* out, int num_cu, hipStream_t s);
 hipError_t launch_mlp_fp8(const moe_handle* h, int F, const void* perm, const void* w1,
                           const float* w1s, const void* w2, const float* w2s, void* act,
                           float* act_scales, void* expert_out, hipStream_t s);

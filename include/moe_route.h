@@ -217,6 +217,18 @@ int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const
                            const void* d_w2, const float* d_w2_scales, void* d_scratch,
                            size_t scratch_bytes, void* d_expert_out, void* stream);
 
+/* The two halves of moe_grouped_swiglu_mlp, for callers that schedule or
+ * time them separately.  FC1 + SwiGLU writes the activations of every kept
+ * row into d_scratch; FC2 reads them from d_scratch and writes d_expert_out.
+ * Arguments and requirements as for moe_grouped_swiglu_mlp; FC2 must run
+ * after FC1 on the same handle and scratch (same stream or ordered). */
+int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
+                           const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
+                           void* d_scratch, size_t scratch_bytes, void* stream);
+int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_w2,
+                    const float* d_w2_scales, const void* d_scratch, size_t scratch_bytes,
+                    void* d_expert_out, void* stream);
+
 /* Combine-unpermute: y[t] = bf16( sum over the token's surviving copies j, in
  * slot order, of p_tj * expert_out[row_id[t,j]] ) accumulated in fp32;
  * p_tj = copy probability if apply_probs else 1; a token with no surviving
