@@ -12,7 +12,7 @@
 // Design (CDNA4, 256 CUs in 8 XCDs, 4 MB L2 per XCD):
 //  * Work unit = (expert, 128 weight rows).  For FC1 the 128 rows are 64 gate
 //    rows and the 64 matching up rows; for FC2 they are 128 output columns.
-//    A unit takes ALL of the expert's rows (in chunks of up to 384 tokens), so
+//    A unit takes ALL of the expert's rows (in chunks of up to 320 tokens), so
 //    a weight row is streamed from HBM once per layer in the common case.
 //  * Experts are dealt to XCDs (expert e -> XCD e mod 8; hardware deals
 //    workgroups round-robin over XCDs, so workgroup b runs on XCD b mod 8).
@@ -23,14 +23,17 @@
 //    ends up with 4 consecutive output features of one token: the epilogue
 //    stores 8 bytes per lane, and the FC1 gate/up values of a feature sit in
 //    the same lane for the SwiGLU.
-//  * Global -> LDS through global_load_lds_dwordx4 (no VGPR staging) into an
-//    NSTAGE-deep ring; the swizzle of 16-byte chunks is chosen on the global
-//    side so MFMA operand reads from LDS are bank-conflict free (64 banks).
+//  * Global -> LDS through global_load_lds_dwordx4 (no VGPR staging): token
+//    slices in a 2-deep ring (they come from L2), weight slices in a 4-deep
+//    ring (from HBM: ~48 KB in flight per CU).  The 16-byte chunk swizzle is
+//    applied on the global side so MFMA operand reads from LDS are bank
+//    conflict free (64 banks).  DMA instructions are interleaved one per MFMA.
 //  * 4 wavefronts; wave w owns token blocks w, w+4, w+8 (32 rows each) and
-//    all 4 weight blocks of the unit: 12 MFMAs per 16-wide K step against 7
-//    LDS fragment reads, the next step's fragments loaded before the current
-//    step's MFMAs issue.  Token blocks past the expert's row count are
-//    skipped.
+//    all 4 weight blocks of the unit: per 16-wide K step 4 weight + up to 3
+//    token fragment reads feed up to 12 MFMAs; the next step's fragments load
+//    while the current step's MFMAs run, and the last step of a stage is
+//    deferred past the next barrier.  Token blocks past the expert's row
+//    count are neither loaded nor multiplied.
 #include "moe_internal.h"
 
 namespace moe {
@@ -141,6 +144,10 @@ __device__ __forceinline__ void mainloop(u32x4* xring, u32x4* wring, const uint1
 #pragma unroll
             for (int q = 0; q < W_LD; ++q) dma_w(st, q);
 
+    // Fragment registers: step s of a stage uses set s&1.  The last step of
+    // stage kt is deferred past the barrier of iteration kt+1, so its MFMAs
+    // keep the matrix pipe busy while stage kt+1's first fragments load.
+    bf16x8 wf[2][4], xf[2][TBW];
     for (int kt = 0; kt < nk; ++kt) {
         // ---- wait for token stage kt and weight stage kt ------------------
         if (kt == 0) {
@@ -158,14 +165,12 @@ __device__ __forceinline__ void mainloop(u32x4* xring, u32x4* wring, const uint1
         const bool more_x = kt + 1 < nk, more_w = kt + WAHEAD < nk;
         const u32x4* xb = xring + (kt & 1) * X_CH;
         const u32x4* wb = wring + (kt % NWSET) * W_CH;
-        bf16x8 wf[2][4], xf[2][TBW];
         auto frags = [&](int s, int buf) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) wf[buf][nb] = __builtin_bit_cast(bf16x8, wb[woff[s][nb]]);
 #pragma unroll
             for (int i = 0; i < NTB; ++i) xf[buf][i] = __builtin_bit_cast(bf16x8, xb[xoff[s][i]]);
         };
-        if (NTB > 0) frags(0, 0);
         // DMA slots in issue order: token q = 0..X_LD-1, then weight q = 0..W_LD-1
         int slot = 0;
         auto next_dma = [&]() {
@@ -176,27 +181,38 @@ __device__ __forceinline__ void mainloop(u32x4* xring, u32x4* wring, const uint1
             }
             ++slot;
         };
+        auto mfmas = [&](int buf, bool with_dma) {
+#pragma unroll
+            for (int i = 0; i < NTB; ++i)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    acc[nb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][nb], xf[buf][i], acc[nb][i], 0, 0, 0);
+                    if (with_dma) next_dma();
+                }
+        };
         if (NTB == 0) {
 #pragma unroll
             for (int d = 0; d < X_LD + W_LD; ++d) next_dma();
         } else {
+            frags(0, 0);
+            if (kt > 0) mfmas((KS - 1) & 1, true);     // deferred last step of stage kt-1
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int cur = s & 1;
-                if (s + 1 < KS) frags(s + 1, cur ^ 1);
-#pragma unroll
-                for (int i = 0; i < NTB; ++i)
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        acc[nb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][nb], xf[cur][i], acc[nb][i],
-                                                                            0, 0, 0);
-                        next_dma();
-                    }
+            for (int s = 0; s < KS - 1; ++s) {
+                frags(s + 1, (s + 1) & 1);
+                mfmas(s & 1, true);
             }
-            // fewer MFMAs than DMA slots (NTB == 1 issues 16 MFMAs; 14 slots)
 #pragma unroll
-            for (int d = KS * 4 * NTB; d < X_LD + W_LD; ++d) next_dma();
+            for (int d = 0; d < X_LD + W_LD; ++d) next_dma();   // slots not yet used (no-op when exhausted)
         }
+    }
+    if (NTB > 0 && nk > 0)
+    {
+#pragma unroll
+        for (int i = 0; i < NTB; ++i)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                acc[nb][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[(KS - 1) & 1][nb], xf[(KS - 1) & 1][i],
+                                                                    acc[nb][i], 0, 0, 0);
     }
     lds_barrier();   // the rings are free before the next chunk / unit refills them
 }
