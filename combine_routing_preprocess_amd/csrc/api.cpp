@@ -226,7 +226,7 @@ size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype) {
     if (wdtype == MOE_BF16) return up(R * (size_t)F * 2, kAlign);
     if (wdtype == MOE_FP8E4M3_B128) {
         if (F % 128) return 0;
-        return up(R * (size_t)F, kAlign) + up(R * (size_t)(F / 128) * 4, kAlign);
+        return up(R * (size_t)F * 4, kAlign);   // fp32 SwiGLU activations
     }
     return 0;
 }
@@ -250,7 +250,9 @@ int check_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* w, con
         if (w_scales) return MOE_EDTYPE;
         if (d.H % 256 || F % 128) return MOE_ESHAPE;
     } else if (wdtype == MOE_FP8E4M3_B128) {
-        return MOE_EUNSUPPORTED;
+        if (!w_scales) return MOE_EINVAL;
+        if (!al4(w_scales)) return MOE_EALIGN;
+        if (d.H % 128 || F % 128) return MOE_ESHAPE;
     } else {
         return MOE_EDTYPE;
     }
@@ -269,6 +271,8 @@ int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const
     if (d_perm_scales) return MOE_EDTYPE;
     if (!d_perm) return MOE_EINVAL;
     if (!al16(d_perm)) return MOE_EALIGN;
+    if (wdtype == MOE_FP8E4M3_B128)
+        return hip_rc(launch_gemm_fp8(h, 0, F, d_perm, d_w1, d_w1_scales, d_scratch, (hipStream_t)stream));
     return hip_rc(launch_gemm_bf16(h, 0, F, d_perm, d_w1, d_scratch, ncu, (hipStream_t)stream));
 }
 
@@ -280,6 +284,8 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
     if (rc) return rc;
     if (!d_expert_out) return MOE_EINVAL;
     if (!al16(d_expert_out)) return MOE_EALIGN;
+    if (wdtype == MOE_FP8E4M3_B128)
+        return hip_rc(launch_gemm_fp8(h, 1, F, d_scratch, d_w2, d_w2_scales, d_expert_out, (hipStream_t)stream));
     return hip_rc(launch_gemm_bf16(h, 1, F, d_scratch, d_w2, d_expert_out, ncu, (hipStream_t)stream));
 }
 

@@ -34,8 +34,9 @@ hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs
 // stage 0: FC1 + SwiGLU (in -> act), stage 1: FC2 (act -> expert_out)
 hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* in, const void* w,
                             void* out, int num_cu, hipStream_t s);
-hipError_t launch_mlp_fp8(const moe_handle* h, int F, const void* perm, const void* w1,
-                          const float* w1s, const void* w2, const float* w2s, void* act,
-                          float* act_scales, void* expert_out, hipStream_t s);
+// stage 0: FC1 + SwiGLU (bf16 rows -> fp32 activations), stage 1: FC2
+// (fp32 activations -> bf16 expert output); e4m3 weights with 128x128 scales
+hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in, const void* w,
+                           const float* ws, void* out, hipStream_t s);
 
 }  // namespace moe

@@ -193,7 +193,8 @@ int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs,
                  int32_t* d_flag, void* stream);
 
 /* Scratch bytes moe_grouped_swiglu_mlp needs for FFN width F and weight
- * dtype wdtype (the FC1 activations of all R rows). 0 if invalid. */
+ * dtype wdtype: the FC1 activations of all R rows (bf16 for MOE_BF16, fp32
+ * for MOE_FP8E4M3_B128, whose FC2 re-quantises them on load). 0 if invalid. */
 size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype);
 
 /* Grouped expert MLP over the permuted rows: for every expert e and every
@@ -208,8 +209,11 @@ size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype);
  *          requires H % 256 == 0 and F % 128 == 0.
  *   wdtype MOE_FP8E4M3_B128: d_w1 [E,2F,H] e4m3, d_w1_scales [E,2F/128,H/128]
  *          fp32, d_w2 [E,H,F] e4m3, d_w2_scales [E,H/128,F/128] fp32; the
- *          bf16 rows are quantised per 1x128 block on load and a is
- *          re-quantised per 1x128 block; requires H, F multiples of 128.
+ *          bf16 rows are quantised per 1x128 block on load (scale = block
+ *          amax / 448, 1 for an all-zero block; code = e4m3(x / scale),
+ *          nearest-even, saturating) and a is re-quantised the same way
+ *          before FC2; requires H, F multiples of 128.  Built for decode-sized
+ *          batches (few rows per expert; weight streaming bound).
  *   d_scratch     >= moe_mlp_scratch_bytes bytes
  *   d_expert_out  [R,H] bf16; rows that hold no kept copy are unspecified */
 int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,

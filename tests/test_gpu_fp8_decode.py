@@ -1,0 +1,132 @@
+"""fp8-weight (W8A8, 128x128 weight-block scales) grouped MLP and the
+decode-sized layer with HIP-graph replay, against the oracle.  Tolerance for
+fp8: per-row relative L2 <= 5e-2."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+import oracle
+from combine_routing_preprocess_amd import Dispatcher
+from gpu_util import DEV, dev, host_bf16, log, rel_l2, row_rel_l2
+
+pytestmark = pytest.mark.gpu
+TOL8 = 5e-2
+
+
+def _check(got_bits, want_bits, what, tol=TOL8):
+    g = S.bf16_to_float(got_bits)
+    w = S.bf16_to_float(want_bits)
+    assert rel_l2(g, w) < tol, (what, rel_l2(g, w))
+    rr = row_rel_l2(g, w)
+    assert rr.max() < tol, (what, rr.max(), int(rr.argmax()))
+
+
+@pytest.mark.parametrize("counts,H,F", [
+    ([0, 1, 15, 17, 70], 256, 256),
+    ([3, 0, 64, 65], 512, 128),
+])
+def test_fp8_mlp_ragged(counts, H, F):
+    E = len(counts)
+    T = int(sum(counts))
+    idx = np.repeat(np.arange(E), counts).astype(np.int16)[:, None]
+    idx = idx[np.random.default_rng(T).permutation(T)]
+    x = S.bf16_normal((T, H), 200 + T)
+    w1q, w1s = S.weights_fp8_blocks(E, 2 * F, H, 201, std=0.05)
+    w2q, w2s = S.weights_fp8_blocks(E, H, F, 202, std=0.05)
+    log("fp8 mlp ragged", counts, H, F)
+    d = Dispatcher(T, H, E, 1, pad_multiple=16)
+    perm, *_ = d.dispatch(dev(x), dev(idx))
+    y = d.grouped_mlp(perm, w1q.to(DEV), w2q.to(DEV), w1_scales=w1s.to(DEV), w2_scales=w2s.to(DEV))
+    torch.cuda.synchronize()
+    rt = oracle.route(idx, 0, E, 1, None, 16, -1, d.R)
+    P = oracle.permute_rows(x, rt["row_id"], d.R)
+    got = host_bf16(y)
+    for e in range(E):
+        s, k = int(rt["seg_off"][e]), int(rt["counts"][e])
+        if k == 0:
+            continue
+        want = oracle.expert_mlp_fp8(P[s:s + k], w1q[e].numpy(), w1s[e].numpy(), w2q[e].numpy(), w2s[e].numpy())
+        _check(got[s:s + k], want, f"expert {e}")
+
+
+@pytest.fixture(scope="module")
+def fp8_weights():
+    """256 experts, H 7168, FFN 2048, e4m3 weights drawn N(0, 0.02) with
+    128x128 block scales (W1 7.5 GB + W2 3.8 GB on the device)."""
+    c = S.CONFIGS["cfg5_decode_fp8"]
+    w1q, w1s = S.weights_fp8_blocks(c.E, 2 * c.F, c.H, c.seed + 1, device=DEV)
+    w2q, w2s = S.weights_fp8_blocks(c.E, c.H, c.F, c.seed + 2, device=DEV)
+    yield c, w1q, w1s, w2q, w2s
+
+
+def _decode_case(c, T):
+    bucket = S.next_pow2_bucket(T)
+    idx, pr = S.route_sigmoid_topk(bucket, c.E, c.K, c.seed + T)
+    x = S.bf16_normal((bucket, c.H), c.seed + T)
+    return bucket, idx, pr, x
+
+
+@pytest.mark.parametrize("T", [16, 100, 256])
+def test_decode_layer_sampled_tokens(fp8_weights, T):
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    bucket, idx, pr, x = _decode_case(c, T)
+    log("fp8 decode layer", T, bucket)
+    d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    tl = torch.tensor([T], dtype=torch.int32, device=DEV)
+    y = d.layer(dev(x), dev(idx), dev(pr), w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl)
+    torch.cuda.synchronize()
+    rt = oracle.route(idx, 0, c.E, c.K, pr, c.pad, -1, d.R, T)
+    assert np.array_equal(d.row_id.cpu().numpy(), rt["row_id"])
+    toks = sorted({0, T - 1, T // 2})
+    want = oracle.layer_tokens(toks, x, rt, lambda e, rows: oracle.expert_mlp_fp8(
+        rows, w1q[e].cpu().numpy(), w1s[e].cpu().numpy(), w2q[e].cpu().numpy(), w2s[e].cpu().numpy()))
+    _check(host_bf16(y[toks]), want, f"T {T}")
+    # tokens past the live count are unrouted: their output is exactly zero
+    if T < bucket:
+        assert torch.count_nonzero(y[T:].float()).item() == 0
+
+
+def test_decode_graph_replay_matches_eager(fp8_weights):
+    """Capture dispatch + FC1 + FC2 + combine once per bucket; replay with new
+    inputs copied into the captured buffers; every replay equals the eager
+    run on the same inputs bit for bit."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    for bucket in (16, 64):
+        log("fp8 decode graph", bucket)
+        d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+        xb = torch.zeros((bucket, c.H), dtype=torch.bfloat16, device=DEV)
+        rb = torch.zeros((bucket, c.K), dtype=torch.int16, device=DEV)
+        pb = torch.zeros((bucket, c.K), dtype=torch.float32, device=DEV)
+        tl = torch.tensor([bucket], dtype=torch.int32, device=DEV)
+        perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+        scratch = d.alloc_mlp_scratch(c.F, "fp8")
+        eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+        yb = torch.empty((bucket, c.H), dtype=torch.bfloat16, device=DEV)
+
+        def step():
+            d.layer(xb, rb, pb, w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl, perm=perm, scratch=scratch,
+                    expert_out=eo, out=yb)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for rep, T in enumerate((bucket, bucket // 2 + 1, 1, 0)):
+            _, idx, pr, x = _decode_case(c, bucket)
+            idx = np.roll(idx, rep, axis=0)
+            xb.copy_(dev(x).view(torch.bfloat16))
+            rb.copy_(dev(idx))
+            pb.copy_(dev(pr))
+            tl.fill_(T)
+            g.replay()
+            torch.cuda.synchronize()
+            replay = yb.clone()
+            step()
+            torch.cuda.synchronize()
+            assert torch.equal(replay.view(torch.int16), yb.view(torch.int16)), (bucket, rep)
+            assert int(d.flag.item()) == 0

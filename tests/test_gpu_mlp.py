@@ -152,3 +152,44 @@ def test_dsv3_combine_from_gpu_expert_out(dsv3_layer):
     Yh[rows] = host_bf16(L["expert_out"][torch.from_numpy(rows).to(DEV)])
     want = oracle.combine_bf16(Yh, rid, rt["copy_prob"][toks])
     _check_rows(host_bf16(L["y"][torch.from_numpy(toks).to(DEV)]), want, "combine")
+
+
+def test_layer_graph_replay_matches_eager():
+    """The bf16 layer captured once in a HIP graph and replayed with new
+    inputs (copied into the captured buffers) equals the eager result bit for
+    bit, replay after replay."""
+    c = S.CONFIGS["cfg1_small_layer"]
+    w1 = dev(S.bf16_normal((c.E, 2 * c.F, c.H), 301, std=0.02)).view(torch.bfloat16)
+    w2 = dev(S.bf16_normal((c.E, c.H, c.F), 302, std=0.02)).view(torch.bfloat16)
+    d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)
+    xb = torch.zeros((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+    rb = torch.zeros((c.T, c.K), dtype=torch.int16, device=DEV)
+    pb = torch.zeros((c.T, c.K), dtype=torch.float32, device=DEV)
+    perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+    scratch = d.alloc_mlp_scratch(c.F)
+    eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+    yb = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        d.layer(xb, rb, pb, w1, w2, perm=perm, scratch=scratch, expert_out=eo, out=yb)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        log("bf16 layer graph replay", rep)
+        idx, pr = S.route_softmax_topk(c.T, c.E, c.K, 400 + rep)
+        xb.copy_(dev(S.bf16_normal((c.T, c.H), 500 + rep)).view(torch.bfloat16))
+        rb.copy_(dev(idx))
+        pb.copy_(dev(pr))
+        g.replay()
+        torch.cuda.synchronize()
+        replay = yb.clone()
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(replay.view(torch.int16), yb.view(torch.int16)), rep
