@@ -59,6 +59,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=16, help="oracle sample size (0 = skip)")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the permute/combine, fp8 routing-stress and decode workloads and a plain copy")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="end with one 1 GiB device copy (reference dispatch for hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -232,6 +236,15 @@ def main() -> int:
                "seconds": round(tc1 - tc0, 2), "gpu_vs_oracle_rel_l2": rel}
         del w1h, w2h
 
+    extra = run_extra(args) if args.extra else None
+    if args.calib_copy:
+        a = torch.empty(2 ** 29, dtype=torch.int16, device=dev)
+        a.fill_(1)
+        bq = torch.empty_like(a)
+        torch.cuda.synchronize()
+        bq.copy_(a)
+        torch.cuda.synchronize()
+
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -246,9 +259,142 @@ def main() -> int:
         "permute_combine": permute_combine,
         "stages": stages,
         "graph_replay": graph,
+        "extra_workloads": extra,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _graph_times(step, reps=30):
+    """Capture `step` in a HIP graph, replay it; min / median ms per replay."""
+    import statistics as st
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        t.append(a.elapsed_time(b))
+    return min(t), st.median(t)
+
+
+def _event_times(fn, reps=30, warm=5):
+    import statistics as st
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        t.append(a.elapsed_time(b))
+    return min(t), st.median(t)
+
+
+def run_extra(args):
+    """The other synthetic workloads, timed on their own (not part of the
+    step above): permute/combine with identity experts, the fp8 routing
+    stress, decode buckets with fp8 weights, and a plain device copy."""
+    import numpy as np
+    import torch
+
+    import moe_synth as S
+    import oracle
+    from combine_routing_preprocess_amd import Dispatcher
+    dev = "cuda"
+    res = {}
+
+    # practical HBM ceiling: a plain 1 GiB device-to-device copy
+    a = torch.empty(2 ** 29, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    mn, md = _event_times(lambda: b.copy_(a))
+    res["device_copy_1GiB"] = {"min_ms": round(mn, 4), "GB_s": round(2 * 2 ** 30 / (mn * 1e-3) / 1e9, 1)}
+    del a, b
+
+    # permute + combine, 8192 x 7168 bf16, 32 experts top-8, capacity 1.5x
+    c = S.CONFIGS["cfg2_permute_combine"]
+    idx, pr = S.route_uniform_distinct(c.T, c.E, c.K, c.seed)
+    mx = int(oracle.route(idx, 0, c.E, c.K, pr)["counts"].max())
+    cap = oracle.capacity_from_rows(mx, 1.5)
+    d = Dispatcher(c.T, c.H, c.E, c.K, capacity=cap)
+    x = torch.from_numpy(S.bf16_normal((c.T, c.H), c.seed).view(np.int16)).to(dev).view(torch.bfloat16)
+    rt, pt = torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev)
+    perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+    d.preprocess(rt, pt)
+    nbytes = (c.T + c.T * c.K) * c.H * 2
+    pm, _ = _event_times(lambda: d.permute(x, out=perm))
+    cm, _ = _event_times(lambda: d.combine(perm, out=y))
+    gm, gmed = _graph_times(lambda: (d.dispatch(x, rt, pt, out=perm), d.combine(perm, out=y)))
+    res["cfg2_permute_combine"] = {
+        "capacity": cap, "permute_min_ms": round(pm, 4), "combine_min_ms": round(cm, 4),
+        "permute_GB_s": round(nbytes / (pm * 1e-3) / 1e9, 1), "combine_GB_s": round(nbytes / (cm * 1e-3) / 1e9, 1),
+        "graph_dispatch_combine_min_ms": round(gm, 4), "graph_median_ms": round(gmed, 4)}
+    del d, x, perm, y
+
+    # routing stress: 256 experts top-36 Zipf, fp8 payload, dense vs Boolean map
+    c = S.CONFIGS["cfg3_route_stress_fp8"]
+    idx, _ = S.route_zipf_gumbel(c.T, c.E, c.K, c.seed)
+    m, _ = S.dense_to_sparse(idx, c.E)
+    xq, xs = S.quantize_rows_fp8_torch(S.bf16_normal((c.T, c.H), c.seed))
+    xq, xs = torch.from_numpy(xq).to(dev), torch.from_numpy(xs).to(dev)
+    out3 = {}
+    for name, routing, fmt in (("dense_i16", idx, "dense_i16"), ("sparse_bool", m, "sparse_bool")):
+        d = Dispatcher(c.T, c.H, c.E, c.K, route_fmt=fmt, payload="fp8")
+        r = torch.from_numpy(routing).to(dev)
+        po = torch.empty((d.R, c.H), dtype=torch.uint8, device=dev)
+        so = torch.empty((d.R, c.H // 128), dtype=torch.float32, device=dev)
+        km, _ = _event_times(lambda: d.preprocess(r))
+        pmn, _ = _event_times(lambda: d.permute(xq, xs, out=po, out_scales=so))
+        nb = (c.T + c.T * c.K) * (c.H + 4 * c.H // 128)
+        out3[name] = {"preprocess_min_us": round(km * 1e3, 1), "permute_min_ms": round(pmn, 4),
+                      "permute_GB_s": round(nb / (pmn * 1e-3) / 1e9, 1)}
+        del d, po, so
+    res["cfg3_route_stress_fp8"] = out3
+
+    # decode buckets, fp8 weights, graph replay of dispatch + FC1 + FC2 + combine
+    c = S.CONFIGS["cfg5_decode_fp8"]
+    w1q, w1s = S.weights_fp8_blocks(c.E, 2 * c.F, c.H, c.seed + 1, device=dev)
+    w2q, w2s = S.weights_fp8_blocks(c.E, c.H, c.F, c.seed + 2, device=dev)
+    per_expert = (2 * c.F * c.H + c.H * c.F) + 4 * (2 * c.F // 128 * c.H // 128 + c.H // 128 * c.F // 128)
+    out5 = {}
+    for T in (16, 64, 256):
+        idx, pr = S.route_sigmoid_topk(T, c.E, c.K, c.seed + T)
+        x = torch.from_numpy(S.bf16_normal((T, c.H), c.seed + T).view(np.int16)).to(dev).view(torch.bfloat16)
+        d = Dispatcher(T, c.H, c.E, c.K, pad_multiple=c.pad)
+        rt, pt = torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev)
+        perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+        scr = d.alloc_mlp_scratch(c.F, "fp8")
+        eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
+        step = lambda: d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, scratch=scr,
+                               expert_out=eo, out=y)
+        gm, gmed = _graph_times(step)
+        touched = int((oracle.route(idx, 0, c.E, c.K, pr, c.pad)["counts"] > 0).sum())
+        wbytes = touched * per_expert
+        out5[f"T{T}"] = {"graph_min_ms": round(gm, 4), "graph_median_ms": round(gmed, 4),
+                         "tokens_per_s": round(T / (gm * 1e-3), 1), "experts_touched": touched,
+                         "weight_GB_s": round(wbytes / (gm * 1e-3) / 1e9, 1)}
+        del d, perm, scr, eo, y
+    res["cfg5_decode_fp8"] = out5
+    return res
 
 
 if __name__ == "__main__":

@@ -30,7 +30,6 @@ are ``uint8`` codes, scales are ``float32``.  Dense routing is ``int16``
 from __future__ import annotations
 
 import dataclasses
-import math
 from typing import Optional
 
 import numpy as np
@@ -217,9 +216,3 @@ def next_pow2_bucket(T: int, floor: int = 16) -> int:
         b *= 2
     return b
 
-
-def capacity_rows(counts: np.ndarray, factor: float) -> int:
-    """Input synthesis helper mirroring the caller-side capacity rule:
-    ceil(max rows x factor) rounded up to a multiple of 4."""
-    c = math.ceil(float(np.max(counts)) * factor)
-    return (c + 3) // 4 * 4
