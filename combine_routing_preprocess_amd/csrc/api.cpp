@@ -225,8 +225,8 @@ size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype) {
     const size_t R = (size_t)h->desc.out_rows;
     if (wdtype == MOE_BF16) return up(R * (size_t)F * 2, kAlign);
     if (wdtype == MOE_FP8E4M3_B128) {
-        if (F % 128) return 0;
-        return up(R * (size_t)F * 4, kAlign);   // fp32 SwiGLU activations
+        if (F % 128 || h->desc.H % 128) return 0;
+        return up(fp8_mlp_scratch_bytes((long long)R, h->desc.H, F), kAlign);
     }
     return 0;
 }
@@ -272,12 +272,12 @@ int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const
     if (!d_perm) return MOE_EINVAL;
     if (!al16(d_perm)) return MOE_EALIGN;
     if (wdtype == MOE_FP8E4M3_B128)
-        return hip_rc(launch_gemm_fp8(h, 0, F, d_perm, d_w1, d_w1_scales, d_scratch, (hipStream_t)stream));
+        return hip_rc(launch_gemm_fp8(h, 0, F, d_perm, d_w1, d_w1_scales, d_scratch, nullptr, (hipStream_t)stream));
     return hip_rc(launch_gemm_bf16(h, 0, F, d_perm, d_w1, d_scratch, ncu, (hipStream_t)stream));
 }
 
 int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_w2,
-                    const float* d_w2_scales, const void* d_scratch, size_t scratch_bytes,
+                    const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
                     void* d_expert_out, void* stream) {
     int ncu = 0;
     int rc = check_mlp(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, &ncu);
@@ -285,7 +285,7 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
     if (!d_expert_out) return MOE_EINVAL;
     if (!al16(d_expert_out)) return MOE_EALIGN;
     if (wdtype == MOE_FP8E4M3_B128)
-        return hip_rc(launch_gemm_fp8(h, 1, F, d_scratch, d_w2, d_w2_scales, d_expert_out, (hipStream_t)stream));
+        return hip_rc(launch_gemm_fp8(h, 1, F, nullptr, d_w2, d_w2_scales, d_scratch, d_expert_out, (hipStream_t)stream));
     return hip_rc(launch_gemm_bf16(h, 1, F, d_scratch, d_w2, d_expert_out, ncu, (hipStream_t)stream));
 }
 

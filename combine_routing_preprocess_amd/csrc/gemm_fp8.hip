@@ -1,6 +1,6 @@
 // Grouped expert MLP with fp8 (OCP e4m3) weights and 128x128 fp32 weight
-// block scales, W8A8: token rows are quantised per 1x128 block on load, the
-// SwiGLU output is re-quantised per 1x128 block on FC2's load.
+// block scales, W8A8: token rows are quantised per 1x128 block before FC1,
+// the SwiGLU output is re-quantised per 1x128 block before FC2.
 //
 // Operation: Megatron-LM PR #6800 "Reuse caller-owned HybridEP dispatch and
 // expert output buffers" (section "Configuration": FP8 expert GEMMs behind the
@@ -10,23 +10,25 @@
 // (1 for an all-zero block), code = e4m3(x / scale), round to nearest even,
 // saturating at 448; dot products use code * scale.
 //
-// Design (decode: few rows per expert, weight streaming bound):
-//  * Work unit = (expert, 64 output features).  One workgroup per unit
+// Design (decode: a few rows per expert, bound by streaming the weights):
+//  * k_quant_rows quantises each row that holds a kept copy once per launch
+//    (16 lanes per 128-column block, 8 values per lane), so the GEMMs only
+//    move codes.  FC1 reads the permuted bf16 rows through it; FC2 reads the
+//    fp32 SwiGLU output of FC1 through it.  Both land in the caller's scratch.
+//  * GEMM work unit = (expert, 64 output features), one workgroup per unit
 //    (experts without rows exit at once); four wavefronts, each owning 16
 //    features: for FC1 its 16 gate rows and the matching 16 up rows, for FC2
-//    16 rows of W2.  A wavefront streams its weight rows straight from HBM to
-//    registers; there is no LDS and no barrier, so latency is hidden by
-//    occupancy (the kernel needs few registers).
+//    16 rows of W2.  A wavefront streams its weight rows straight from HBM
+//    into registers, kU 128-wide K blocks per group so several KB per
+//    wavefront are in flight; there is no LDS and no barrier, latency is
+//    hidden by the in-flight loads and by occupancy.
 //  * v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales) computes one 128-wide K
-//    block per instruction: weights are the A operand (16 rows), tokens the B
-//    operand (16 columns).  Lane l supplies row/column l%16 and the 32 K
-//    values (l/16)*32 .. +31 of the block for both operands, so the 16x16
-//    block product is exact; its result is multiplied by weight scale x token
-//    scale and added into fp32 accumulators (lane l holds column l%16, rows
+//    block per instruction: weights are the A operand (16 rows), token codes
+//    the B operand (16 columns).  Lane l supplies row/column l%16 and bytes
+//    (l/16)*32 .. +31 of the block for both operands, so the 16x16 block
+//    product is exact; it is multiplied by weight scale x token scale and
+//    added into fp32 accumulators (lane l holds column l%16, rows
 //    4*(l/16) + i).
-//  * Token quantisation on load: the four lanes holding a token's 128 values
-//    of a block combine their maxima with two xor-shuffles, then each converts
-//    its 32 values (fp32 divide, hardware e4m3 conversion after clamping).
 //  * Up to 4 token blocks (64 rows) per pass; more rows take more passes.
 #include "moe_internal.h"
 
@@ -38,52 +40,65 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxTB = 4;         // token blocks (16 rows) per pass
 constexpr int kFeat = 64;         // output features per unit
+constexpr int kU = 4;             // 128-wide K blocks per load group
 
 __device__ __forceinline__ float e4m3_prep(float v) {   // saturate to the e4m3 range
     return fminf(fmaxf(v, -448.f), 448.f);
 }
 
-// 32 values of one lane (fp32) -> 32 e4m3 codes for the MFMA operand, with
-// the 128-wide block scale shared by the 4 lanes l, l^16, l^32, l^48.
-__device__ __forceinline__ i32x8 quant32(const float (&v)[32], float& scale) {
-    float amax = 0.f;
+// ---- row quantiser ------------------------------------------------------------
+// Rows r with src_row[r] >= 0 (rows that hold a kept copy): src [R, ncols]
+// (bf16 bit patterns or fp32) -> q [R, ncols] e4m3 codes, qs [R, ncols/128]
+// scales.  One wavefront per row; 16 lanes per 128-column block, 8 values
+// per lane, 4 blocks per step.
+template <typename SRC>
+__global__ __launch_bounds__(256) void k_quant_rows(const SRC* __restrict__ src, int ncols, long long R,
+                                                    const int32_t* __restrict__ src_row, uint8_t* __restrict__ q,
+                                                    float* __restrict__ qs) {
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= R || src_row[row] < 0) return;
+    const int nb = ncols / 128;
+    const int g = lane >> 4, l16 = lane & 15;
+    const SRC* s = src + (size_t)row * ncols;
+    uint8_t* qr = q + (size_t)row * ncols;
+    for (int b0 = 0; b0 < nb; b0 += 4) {
+        const int b = b0 + g;
+        if (b < nb) {                       // whole 16-lane groups are active or not
+            float v[8];
+            const size_t c = (size_t)b * 128 + l16 * 8;
+            if constexpr (sizeof(SRC) == 2) {
+                const u32x4 w = *(const u32x4*)(s + c);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float s = amax > 0.f ? amax / 448.f : 1.f;
-    scale = s;
-    i32x8 q;
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = bf16_lo(w[i]);
+                    v[2 * i + 1] = bf16_hi(w[i]);
+                }
+            } else {
+                const float4 a = *(const float4*)(s + c), bb = *(const float4*)(s + c + 4);
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
+            }
+            float amax = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-        int p = 0;
-        p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[4 * w + 0] / s), e4m3_prep(v[4 * w + 1] / s), p, false);
-        p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[4 * w + 2] / s), e4m3_prep(v[4 * w + 3] / s), p, true);
-        q[w] = p;
-    }
-    return q;
-}
-
-__device__ __forceinline__ void load_bf16x32(const uint16_t* p, float (&v)[32]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const u32x4 w = *(const u32x4*)(p + 8 * c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[8 * c + 2 * i] = bf16_lo(w[i]);
-            v[8 * c + 2 * i + 1] = bf16_hi(w[i]);
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            amax = fmaxf(amax, __shfl_xor(amax, 4));
+            amax = fmaxf(amax, __shfl_xor(amax, 8));
+            const float sc = amax > 0.f ? amax / 448.f : 1.f;
+            uint2 out;
+            int p = 0;
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[0] / sc), e4m3_prep(v[1] / sc), p, false);
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[2] / sc), e4m3_prep(v[3] / sc), p, true);
+            out.x = (uint32_t)p;
+            p = 0;
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[4] / sc), e4m3_prep(v[5] / sc), p, false);
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[6] / sc), e4m3_prep(v[7] / sc), p, true);
+            out.y = (uint32_t)p;
+            *(uint2*)(qr + c) = out;
+            if (l16 == 0) qs[(size_t)row * nb + b] = sc;
         }
-    }
-}
-
-__device__ __forceinline__ void load_f32x32(const float* p, float (&v)[32]) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const float4 w = *(const float4*)(p + 4 * c);
-        v[4 * c] = w.x;
-        v[4 * c + 1] = w.y;
-        v[4 * c + 2] = w.z;
-        v[4 * c + 3] = w.w;
     }
 }
 
@@ -97,14 +112,93 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
 }
 
-// MODE 0: FC1 + SwiGLU.  X = permuted bf16 rows [R,H]; W = W1 [E,2F,H] e4m3,
-//         Ws = [E,2F/128,H/128]; Out = fp32 activations [R,F].
-// MODE 1: FC2.  X = fp32 activations [R,F]; W = W2 [E,H,F] e4m3,
-//         Ws = [E,H/128,F/128]; Out = bf16 expert output [R,H].
+// One pass over up to 16*NTB rows (m0 .. m0+mv-1 of the segment) for this
+// wavefront's 16 features; NTB token blocks of 16 rows.
+template <int MODE, int NTB>
+__device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const float* __restrict__ Xs,
+                                         const uint8_t* wg, const uint8_t* wu, const float* sg, const float* su,
+                                         void* __restrict__ Outv, long long seg, int m0, int mv, int Kdim, int Nout,
+                                         int f0, int lane) {
+    constexpr int U = MODE == 0 ? kU : 2 * kU;   // K blocks per group (FC2 loads half as much per block)
+    const int kq = (lane >> 4) * 32;
+    const int nkb = Kdim / 128;
+    f32x4 acc_g[NTB], acc_u[NTB];
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) {
+        acc_g[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_u[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // token row of this lane in block t: m0 + 16t + lane%16 (clamped)
+    size_t xrow[NTB];
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) xrow[t] = (size_t)(seg + m0 + min(16 * t + (lane & 15), mv - 1));
+
+    // one group of UU K blocks: the weights of all of them are loaded first
+    auto group = [&](int kb0, auto uc) {
+        constexpr int UU = decltype(uc)::value;
+        i32x8 a_g[UU], a_u[UU];
+        float s_g[UU], s_u[UU];
+#pragma unroll
+        for (int u = 0; u < UU; ++u) {
+            a_g[u] = load_fp8x32(wg + (size_t)(kb0 + u) * 128);
+            if (MODE == 0) a_u[u] = load_fp8x32(wu + (size_t)(kb0 + u) * 128);
+            s_g[u] = sg[kb0 + u];
+            s_u[u] = MODE == 0 ? su[kb0 + u] : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < NTB; ++t) {
+#pragma unroll
+            for (int u = 0; u < UU; ++u) {
+                const i32x8 bq = load_fp8x32(Xq + xrow[t] * Kdim + (size_t)(kb0 + u) * 128 + kq);
+                const float sx = Xs[xrow[t] * nkb + kb0 + u];
+                const f32x4 pg = mfma_fp8(a_g[u], bq);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc_g[t][i] = fmaf(pg[i], s_g[u] * sx, acc_g[t][i]);
+                if (MODE == 0) {
+                    const f32x4 pu = mfma_fp8(a_u[u], bq);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc_u[t][i] = fmaf(pu[i], s_u[u] * sx, acc_u[t][i]);
+                }
+            }
+        }
+    };
+    int kb = 0;
+    for (; kb + U <= nkb; kb += U) group(kb, std::integral_constant<int, U>{});
+    for (; kb < nkb; ++kb) group(kb, std::integral_constant<int, 1>{});
+
+    // ---- epilogue: lane holds token m0+16t+lane%16, features f0+4*(lane/16)+i
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) {
+        const int tok = 16 * t + (lane & 15);
+        if (tok >= mv) continue;
+        const size_t orow = (size_t)(seg + m0 + tok) * Nout + f0 + 4 * (lane >> 4);
+        if (MODE == 0) {
+            float4 o;
+            float a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float g = acc_g[t][i], u = acc_u[t][i];
+                a[i] = g / (1.f + __expf(-g)) * u;
+            }
+            o.x = a[0]; o.y = a[1]; o.z = a[2]; o.w = a[3];
+            *(float4*)((float*)Outv + orow) = o;
+        } else {
+            uint2 o;
+            o.x = f32_to_bf16(acc_g[t][0]) | (f32_to_bf16(acc_g[t][1]) << 16);
+            o.y = f32_to_bf16(acc_g[t][2]) | (f32_to_bf16(acc_g[t][3]) << 16);
+            *(uint2*)((uint16_t*)Outv + orow) = o;
+        }
+    }
+}
+
+// MODE 0: FC1 + SwiGLU.  Xq/Xs = quantised permuted rows [R,H] / [R,H/128];
+//         W = W1 [E,2F,H] e4m3, Ws = [E,2F/128,H/128]; Out = fp32 [R,F].
+// MODE 1: FC2.  Xq/Xs = quantised activations [R,F] / [R,F/128]; W = W2
+//         [E,H,F] e4m3, Ws = [E,H/128,F/128]; Out = bf16 expert output [R,H].
 template <int MODE>
-__global__ __launch_bounds__(256) void k_gemm_fp8(const void* __restrict__ Xv, const uint8_t* __restrict__ W,
-                                                  const float* __restrict__ Ws, void* __restrict__ Outv,
-                                                  const int64_t* __restrict__ seg_off,
+__global__ __launch_bounds__(256) void k_gemm_fp8(const uint8_t* __restrict__ Xq, const float* __restrict__ Xs,
+                                                  const uint8_t* __restrict__ W, const float* __restrict__ Ws,
+                                                  void* __restrict__ Outv, const int64_t* __restrict__ seg_off,
                                                   const int32_t* __restrict__ kept, long long R, int Kdim,
                                                   int Wrows, int Nout, int units_per_expert) {
     const int e = blockIdx.x / units_per_expert;
@@ -116,96 +210,61 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(const void* __restrict__ Xv, c
     if (me <= 0) return;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kq = (lane >> 4) * 32;                  // this lane's 32 K values inside a 128 block
+    const int kq = (lane >> 4) * 32;                  // this lane's 32 bytes inside a 128 block
     const int nkb = Kdim / 128;
     const int f0 = unit * kFeat + wave * 16;          // first output feature of this wavefront
-    const int ksb = Kdim / 128;                        // scale blocks along K
     // weight rows of this lane: gate (and up) row f0 + lane%16
     const int r_g = f0 + (lane & 15);
     const uint8_t* wg = W + ((size_t)e * Wrows + r_g) * Kdim + kq;
     const uint8_t* wu = W + ((size_t)e * Wrows + (MODE == 0 ? Nout + r_g : r_g)) * Kdim + kq;
-    const float* sg = Ws + ((size_t)e * (Wrows / 128) + f0 / 128) * ksb;
-    const float* su = Ws + ((size_t)e * (Wrows / 128) + (MODE == 0 ? (Nout + f0) / 128 : f0 / 128)) * ksb;
+    const float* sg = Ws + ((size_t)e * (Wrows / 128) + f0 / 128) * nkb;
+    const float* su = Ws + ((size_t)e * (Wrows / 128) + (MODE == 0 ? (Nout + f0) / 128 : f0 / 128)) * nkb;
 
     for (int m0 = 0; m0 < me; m0 += 16 * kMaxTB) {
         const int mv = min(16 * kMaxTB, me - m0);
-        const int ntb = (mv + 15) / 16;
-        f32x4 acc_g[kMaxTB], acc_u[kMaxTB];
-#pragma unroll
-        for (int t = 0; t < kMaxTB; ++t) {
-            acc_g[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc_u[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        // token row of this lane in block t: m0 + 16t + lane%16 (clamped)
-        size_t xrow[kMaxTB];
-#pragma unroll
-        for (int t = 0; t < kMaxTB; ++t)
-            xrow[t] = (size_t)(seg + m0 + min(16 * t + (lane & 15), mv - 1)) * Kdim + kq;
-
-        for (int kb = 0; kb < nkb; ++kb) {
-            const i32x8 a_g = load_fp8x32(wg + kb * 128);
-            i32x8 a_u;
-            if (MODE == 0) a_u = load_fp8x32(wu + kb * 128);
-            const float s_g = sg[kb];
-            const float s_u = MODE == 0 ? su[kb] : 0.f;
-#pragma unroll
-            for (int t = 0; t < kMaxTB; ++t) {
-                if (t >= ntb) break;
-                float v[32];
-                if (MODE == 0) load_bf16x32((const uint16_t*)Xv + xrow[t] + kb * 128, v);
-                else load_f32x32((const float*)Xv + xrow[t] + kb * 128, v);
-                float sx;
-                const i32x8 bq = quant32(v, sx);
-                const f32x4 pg = mfma_fp8(a_g, bq);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc_g[t][i] = fmaf(pg[i], s_g * sx, acc_g[t][i]);
-                if (MODE == 0) {
-                    const f32x4 pu = mfma_fp8(a_u, bq);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc_u[t][i] = fmaf(pu[i], s_u * sx, acc_u[t][i]);
-                }
-            }
-        }
-        // ---- epilogue: lane holds token m0+16t+lane%16, features f0+4*(lane/16)+i
-#pragma unroll
-        for (int t = 0; t < kMaxTB; ++t) {
-            const int tok = 16 * t + (lane & 15);
-            if (t >= ntb || tok >= mv) continue;
-            const size_t orow = (size_t)(seg + m0 + tok) * Nout + f0 + 4 * (lane >> 4);
-            if (MODE == 0) {
-                float4 o;
-                float a[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float g = acc_g[t][i], u = acc_u[t][i];
-                    a[i] = g / (1.f + __expf(-g)) * u;
-                }
-                o.x = a[0]; o.y = a[1]; o.z = a[2]; o.w = a[3];
-                *(float4*)((float*)Outv + orow) = o;
-            } else {
-                uint2 o;
-                o.x = f32_to_bf16(acc_g[t][0]) | (f32_to_bf16(acc_g[t][1]) << 16);
-                o.y = f32_to_bf16(acc_g[t][2]) | (f32_to_bf16(acc_g[t][3]) << 16);
-                *(uint2*)((uint16_t*)Outv + orow) = o;
-            }
+        switch ((mv + 15) / 16) {
+            case 1: fp8_pass<MODE, 1>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
+            case 2: fp8_pass<MODE, 2>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
+            case 3: fp8_pass<MODE, 3>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
+            default: fp8_pass<MODE, 4>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
         }
     }
 }
 
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 }  // namespace
 
+// Scratch of the fp8 path, in this order: fp32 SwiGLU activations [R,F],
+// token codes [R,H] and scales [R,H/128], activation codes [R,F] and scales
+// [R,F/128]; each region starts on a 256-byte boundary.
+size_t fp8_mlp_scratch_bytes(long long R, int H, int F) {
+    const size_t r = (size_t)R;
+    return up256(r * F * 4) + up256(r * H) + up256(r * (H / 128) * 4) + up256(r * F) + up256(r * (F / 128) * 4);
+}
+
 hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in, const void* w,
-                           const float* ws, void* out, hipStream_t s) {
+                           const float* ws, void* scratch, void* out, hipStream_t s) {
     const moe_desc& d = h->desc;
     const long long R = d.out_rows;
     if (R == 0) return hipSuccess;
+    char* base = (char*)scratch;
+    float* act = (float*)base;
+    uint8_t* xq = (uint8_t*)(base + up256((size_t)R * F * 4));
+    float* xs = (float*)((char*)xq + up256((size_t)R * d.H));
+    uint8_t* aq = (uint8_t*)((char*)xs + up256((size_t)R * (d.H / 128) * 4));
+    float* as = (float*)((char*)aq + up256((size_t)R * F));
+    const int qgrid = (int)((R + 3) / 4);
     if (stage == 0) {
+        hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(qgrid), dim3(256), 0, s, (const uint16_t*)in, d.H, R,
+                           h->src_row, xq, xs);
         const int upe = F / kFeat;
-        hipLaunchKernelGGL(k_gemm_fp8<0>, dim3(d.E * upe), dim3(256), 0, s, in, (const uint8_t*)w, ws, out,
+        hipLaunchKernelGGL(k_gemm_fp8<0>, dim3(d.E * upe), dim3(256), 0, s, xq, xs, (const uint8_t*)w, ws, act,
                            h->seg_off, h->kept, R, d.H, 2 * F, F, upe);
     } else {
+        hipLaunchKernelGGL(k_quant_rows<float>, dim3(qgrid), dim3(256), 0, s, act, F, R, h->src_row, aq, as);
         const int upe = d.H / kFeat;
-        hipLaunchKernelGGL(k_gemm_fp8<1>, dim3(d.E * upe), dim3(256), 0, s, in, (const uint8_t*)w, ws, out,
+        hipLaunchKernelGGL(k_gemm_fp8<1>, dim3(d.E * upe), dim3(256), 0, s, aq, as, (const uint8_t*)w, ws, out,
                            h->seg_off, h->kept, R, F, d.H, d.H, upe);
     }
     return hipGetLastError();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_route.h"
 
 namespace moe {
@@ -36,7 +38,10 @@ hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* i
                             void* out, int num_cu, hipStream_t s);
 // stage 0: FC1 + SwiGLU (bf16 rows -> fp32 activations), stage 1: FC2
 // (fp32 activations -> bf16 expert output); e4m3 weights with 128x128 scales
+// fp8 path: stage 0 quantises the permuted rows `in` into the scratch and
+// writes fp32 activations there; stage 1 quantises those and writes `out`.
 hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in, const void* w,
-                           const float* ws, void* out, hipStream_t s);
+                           const float* ws, void* scratch, void* out, hipStream_t s);
+size_t fp8_mlp_scratch_bytes(long long R, int H, int F);
 
 }  // namespace moe

@@ -193,8 +193,10 @@ int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs,
                  int32_t* d_flag, void* stream);
 
 /* Scratch bytes moe_grouped_swiglu_mlp needs for FFN width F and weight
- * dtype wdtype: the FC1 activations of all R rows (bf16 for MOE_BF16, fp32
- * for MOE_FP8E4M3_B128, whose FC2 re-quantises them on load). 0 if invalid. */
+ * dtype wdtype: MOE_BF16 holds the bf16 FC1 activations of all R rows;
+ * MOE_FP8E4M3_B128 holds the fp32 FC1 activations plus the e4m3 codes and
+ * fp32 1x128 scales of the permuted rows and of the activations (each input
+ * is quantised once per call).  0 if invalid. */
 size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype);
 
 /* Grouped expert MLP over the permuted rows: for every expert e and every
@@ -223,14 +225,16 @@ int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const
 
 /* The two halves of moe_grouped_swiglu_mlp, for callers that schedule or
  * time them separately.  FC1 + SwiGLU writes the activations of every kept
- * row into d_scratch; FC2 reads them from d_scratch and writes d_expert_out.
+ * row into d_scratch; FC2 reads them from d_scratch (with fp8 weights it
+ * first writes their 1x128 codes and scales into d_scratch as well) and
+ * writes d_expert_out.
  * Arguments and requirements as for moe_grouped_swiglu_mlp; FC2 must run
  * after FC1 on the same handle and scratch (same stream or ordered). */
 int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
                            const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
                            void* d_scratch, size_t scratch_bytes, void* stream);
 int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_w2,
-                    const float* d_w2_scales, const void* d_scratch, size_t scratch_bytes,
+                    const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
                     void* d_expert_out, void* stream);
 
 /* Combine-unpermute: y[t] = bf16( sum over the token's surviving copies j, in
