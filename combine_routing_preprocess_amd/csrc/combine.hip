@@ -8,9 +8,12 @@
 // #16190 "Update CuTeDSL MegaMoE kernels" (review-fix commit: the per-token
 // top-k reduction, which must cope with an empty token set).
 //
-// Token-major: one wavefront per token; each lane owns 16-byte column chunks
-// and sums the token's copies in slot order with fused multiply-adds, so the
-// result does not depend on scheduling.  Expert-output rows are read once
+// Token-major: a token's row is cut into `nsplit` column slices (one for
+// large batches, more when there are few tokens so that enough wavefronts
+// run); one wavefront per (token, slice).  Each lane owns 16-byte column
+// chunks and sums the token's copies in slot order with fused multiply-adds,
+// so the result does not depend on scheduling.  The loads of four copies are
+// issued before their multiply-adds.  Expert-output rows are read once
 // (non-temporal); output rows are written once.
 #include "moe_internal.h"
 
@@ -18,45 +21,59 @@ namespace moe {
 namespace {
 
 constexpr int kCombU = 4;   // 16-byte chunks per lane per pass
+constexpr int kCombJ = 4;   // copies loaded ahead of their multiply-adds
 
 __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ Y, int T, int K, int nch, int R,
-                                                 const int32_t* __restrict__ row_id,
+                                                 int nsplit, int slice_ch, const int32_t* __restrict__ row_id,
                                                  const float* __restrict__ copy_prob, int apply,
                                                  u32x4* __restrict__ y) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = wv / nsplit;
     if (t >= T) return;
+    const int cs = (wv - t * nsplit) * slice_ch;
+    const int ce = min(nch, cs + slice_ch);
     const int32_t* rid = row_id + (size_t)t * K;
     const float* cp = copy_prob + (size_t)t * K;
-    for (int c0 = 0; c0 < nch; c0 += 64 * kCombU) {
+    for (int c0 = cs; c0 < ce; c0 += 64 * kCombU) {
         float acc[kCombU][8];
 #pragma unroll
         for (int u = 0; u < kCombU; ++u)
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
-        for (int j = 0; j < K; ++j) {
-            const int r = rid[j];
-            if (r < 0 || r >= R) continue;
-            const float p = apply ? cp[j] : 1.f;
-            const u32x4* src = Y + (size_t)r * nch;
-            u32x4 v[kCombU];
+        for (int j0 = 0; j0 < K; j0 += kCombJ) {
+            u32x4 v[kCombJ][kCombU];
+            float pj[kCombJ];
+            bool ok[kCombJ];
 #pragma unroll
-            for (int u = 0; u < kCombU; ++u) {
-                const int c = c0 + u * 64 + lane;
-                v[u] = c < nch ? __builtin_nontemporal_load(src + c) : u32x4{0u, 0u, 0u, 0u};
+            for (int jj = 0; jj < kCombJ; ++jj) {
+                const int j = j0 + jj;
+                const int r = j < K ? rid[j] : -1;
+                ok[jj] = r >= 0 && r < R;
+                pj[jj] = ok[jj] ? (apply ? cp[j] : 1.f) : 0.f;
+                const u32x4* src = Y + (size_t)(ok[jj] ? r : 0) * nch;
+#pragma unroll
+                for (int u = 0; u < kCombU; ++u) {
+                    const int c = c0 + u * 64 + lane;
+                    v[jj][u] = (ok[jj] && c < ce) ? __builtin_nontemporal_load(src + c) : u32x4{0u, 0u, 0u, 0u};
+                }
             }
 #pragma unroll
-            for (int u = 0; u < kCombU; ++u)
+            for (int jj = 0; jj < kCombJ; ++jj) {
+                if (!ok[jj]) continue;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    acc[u][2 * w] = fmaf(p, bf16_lo(v[u][w]), acc[u][2 * w]);
-                    acc[u][2 * w + 1] = fmaf(p, bf16_hi(v[u][w]), acc[u][2 * w + 1]);
-                }
+                for (int u = 0; u < kCombU; ++u)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        acc[u][2 * w] = fmaf(pj[jj], bf16_lo(v[jj][u][w]), acc[u][2 * w]);
+                        acc[u][2 * w + 1] = fmaf(pj[jj], bf16_hi(v[jj][u][w]), acc[u][2 * w + 1]);
+                    }
+            }
         }
 #pragma unroll
         for (int u = 0; u < kCombU; ++u) {
             const int c = c0 + u * 64 + lane;
-            if (c < nch) {
+            if (c < ce) {
                 u32x4 o;
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
@@ -74,8 +91,11 @@ hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs
     const moe_desc& d = h->desc;
     if (d.T == 0) return hipSuccess;
     const int nch = d.H * 2 / 16;
-    hipLaunchKernelGGL(k_combine, dim3((d.T + 3) / 4), dim3(256), 0, s, (const u32x4*)y_in, d.T, d.K, nch,
-                       (int)d.out_rows, h->row_id, h->copy_prob, apply_probs, (u32x4*)y_out);
+    int nsplit, slice_ch;
+    row_slices(d.T, nch, &nsplit, &slice_ch);
+    const long long waves = (long long)d.T * nsplit;
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, (const u32x4*)y_in, d.T, d.K,
+                       nch, (int)d.out_rows, nsplit, slice_ch, h->row_id, h->copy_prob, apply_probs, (u32x4*)y_out);
     return hipGetLastError();
 }
 

@@ -24,9 +24,10 @@
 //    hidden by the in-flight loads and by occupancy.
 //  * v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales) computes one 128-wide K
 //    block per instruction: weights are the A operand (16 rows), token codes
-//    the B operand (16 columns).  Lane l supplies row/column l%16 and bytes
-//    (l/16)*32 .. +31 of the block for both operands, so the 16x16 block
-//    product is exact; it is multiplied by weight scale x token scale and
+//    the B operand (16 columns).  Lane l supplies row/column l%16 and the
+//    same 32 bytes of the block for both operands (two 16-byte pieces 64
+//    bytes apart, so each load instruction reads 64 contiguous bytes per
+//    row); the 16x16 block product is exact; it is multiplied by weight scale x token scale and
 //    added into fp32 accumulators (lane l holds column l%16, rows
 //    4*(l/16) + i).
 //  * Up to 4 token blocks (64 rows) per pass; more rows take more passes.
@@ -102,8 +103,12 @@ __global__ __launch_bounds__(256) void k_quant_rows(const SRC* __restrict__ src,
     }
 }
 
+// The 32 operand bytes of a lane in a 128-wide K block: bytes kq..kq+15 and
+// kq+64..kq+79 with kq = 16*(lane/16).  Weights and tokens use the same K
+// assignment, so each 128-byte block is covered exactly once, and one load
+// instruction reads 64 contiguous bytes of each of its 16 rows.
 __device__ __forceinline__ i32x8 load_fp8x32(const uint8_t* p) {
-    const u32x4 a = *(const u32x4*)p, b = *(const u32x4*)(p + 16);
+    const u32x4 a = *(const u32x4*)p, b = *(const u32x4*)(p + 64);
     return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
@@ -120,7 +125,7 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
                                          void* __restrict__ Outv, long long seg, int m0, int mv, int Kdim, int Nout,
                                          int f0, int lane) {
     constexpr int U = MODE == 0 ? kU : 2 * kU;   // K blocks per group (FC2 loads half as much per block)
-    const int kq = (lane >> 4) * 32;
+    const int kq = (lane >> 4) * 16;
     const int nkb = Kdim / 128;
     f32x4 acc_g[NTB], acc_u[NTB];
 #pragma unroll
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(const uint8_t* __restrict__ Xq
     if (me <= 0) return;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kq = (lane >> 4) * 32;                  // this lane's 32 bytes inside a 128 block
+    const int kq = (lane >> 4) * 16;                  // this lane's 32 bytes inside a 128 block
     const int nkb = Kdim / 128;
     const int f0 = unit * kFeat + wave * 16;          // first output feature of this wavefront
     // weight rows of this lane: gate (and up) row f0 + lane%16

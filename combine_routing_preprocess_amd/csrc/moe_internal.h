@@ -29,6 +29,19 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 hipError_t launch_route(const moe_handle* h, const void* routing, const float* probs,
                         const int32_t* T_live, int32_t* tokens_per_expert, float* out_probs,
                         int32_t* flag, hipStream_t s);
+// Column slices per token row for the row-copy kernels: one wavefront per
+// (token, slice).  Few tokens get more slices (whole 64-chunk groups) so that
+// at least ~4096 wavefronts run; large batches keep one slice per row.
+inline void row_slices(int T, int nch, int* nsplit, int* slice_ch) {
+    const int groups = (nch + 63) / 64;
+    int n = T > 0 ? (4096 + T - 1) / T : 1;
+    if (n > groups) n = groups;
+    if (n < 1) n = 1;
+    const int gps = (groups + n - 1) / n;          // 64-chunk groups per slice
+    *slice_ch = gps * 64;
+    *nsplit = (nch + *slice_ch - 1) / *slice_ch;
+}
+
 hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_scales, void* out,
                           float* out_scales, hipStream_t s);
 hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs, void* y_out,

@@ -6,12 +6,14 @@
 // reuse HybridEP routing allgather buffer" (section "Full HybridEP reference
 // validation": dispatch with permutation for BF16 and FP8 payloads).
 //
-// Token-major: one wavefront owns one token, reads its row once into
-// registers (16-byte loads) and stores it to each of its k destinations, so
+// Token-major: a token's row is cut into `nsplit` column slices (one for
+// large batches, more when there are few tokens so that enough wavefronts
+// run); one wavefront per (token, slice) reads its slice once into registers
+// (16-byte loads) and stores it to each of the token's k destinations, so
 // HBM sees the algorithmic minimum, T row reads + (kept copies) row writes.
 // Row reads and writes bypass cache residency (non-temporal): the permuted
 // buffer is far larger than the last-level cache and is consumed by another
-// kernel.  fp8 rows carry their per-128-column fp32 scales along.
+// kernel.  fp8 rows carry their per-128-column fp32 scales along (slice 0).
 #include "moe_internal.h"
 
 namespace moe {
@@ -20,20 +22,24 @@ namespace {
 constexpr int kPermU = 7;   // 16-byte chunks held per lane per pass
 
 __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, int T, int K, int nch, int R,
-                                                 const int32_t* __restrict__ row_id,
+                                                 int nsplit, int slice_ch, const int32_t* __restrict__ row_id,
                                                  u32x4* __restrict__ out, const float* __restrict__ xs,
                                                  float* __restrict__ outs, int nsc) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = wv / nsplit;
     if (t >= T) return;
+    const int sl = wv - t * nsplit;
+    const int cs = sl * slice_ch;
+    const int ce = min(nch, cs + slice_ch);
     const u32x4* src = x + (size_t)t * nch;
     const int32_t* rid = row_id + (size_t)t * K;
-    for (int c0 = 0; c0 < nch; c0 += 64 * kPermU) {
+    for (int c0 = cs; c0 < ce; c0 += 64 * kPermU) {
         u32x4 v[kPermU];
 #pragma unroll
         for (int u = 0; u < kPermU; ++u) {
             const int c = c0 + u * 64 + lane;
-            if (c < nch) v[u] = __builtin_nontemporal_load(src + c);
+            if (c < ce) v[u] = __builtin_nontemporal_load(src + c);
         }
         for (int j = 0; j < K; ++j) {
             const int r = rid[j];
@@ -42,11 +48,11 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
 #pragma unroll
             for (int u = 0; u < kPermU; ++u) {
                 const int c = c0 + u * 64 + lane;
-                if (c < nch) __builtin_nontemporal_store(v[u], dst + c);
+                if (c < ce) __builtin_nontemporal_store(v[u], dst + c);
             }
         }
     }
-    if (xs) {
+    if (xs && sl == 0) {
         for (int j = 0; j < K; ++j) {
             const int r = rid[j];
             if (r < 0 || r >= R) continue;
@@ -65,8 +71,12 @@ hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_sca
     const int row_bytes = fp8 ? d.H : d.H * 2;
     const int nch = row_bytes / 16;
     const int nsc = fp8 ? d.H / 128 : 0;
-    hipLaunchKernelGGL(k_permute, dim3((d.T + 3) / 4), dim3(256), 0, s, (const u32x4*)x, d.T, d.K, nch,
-                       (int)d.out_rows, h->row_id, (u32x4*)out, fp8 ? x_scales : nullptr, fp8 ? out_scales : nullptr, nsc);
+    int nsplit, slice_ch;
+    row_slices(d.T, nch, &nsplit, &slice_ch);
+    const long long waves = (long long)d.T * nsplit;
+    hipLaunchKernelGGL(k_permute, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, (const u32x4*)x, d.T, d.K, nch,
+                       (int)d.out_rows, nsplit, slice_ch, h->row_id, (u32x4*)out, fp8 ? x_scales : nullptr,
+                       fp8 ? out_scales : nullptr, nsc);
     return hipGetLastError();
 }
 
