@@ -15,10 +15,11 @@
 //    (16 lanes per 128-column block, 8 values per lane), so the GEMMs only
 //    move codes.  FC1 reads the permuted bf16 rows through it; FC2 reads the
 //    fp32 SwiGLU output of FC1 through it.  Both land in the caller's scratch.
-//  * GEMM work unit = (expert, 64 output features), one workgroup per unit
-//    (experts without rows exit at once); four wavefronts, each owning 16
-//    features: for FC1 its 16 gate rows and the matching 16 up rows, for FC2
-//    16 rows of W2.  A wavefront streams its weight rows straight from HBM
+//  * GEMM work unit = (expert, 64 features) for FC1 and (expert, 128 output
+//    rows) for FC2, one workgroup per unit (experts without rows exit at
+//    once); four wavefronts, each owning two 16-row weight tiles: for FC1 the
+//    16 gate rows and the matching 16 up rows of 16 features, for FC2 32
+//    consecutive rows of W2.  A wavefront streams its weight rows straight from HBM
 //    into registers, kU 128-wide K blocks per group so several KB per
 //    wavefront are in flight; there is no LDS and no barrier, latency is
 //    hidden by the in-flight loads and by occupancy.
@@ -40,7 +41,8 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxTB = 4;         // token blocks (16 rows) per pass
-constexpr int kFeat = 64;         // output features per unit
+constexpr int kFeat = 64;         // FC1: features per unit (16 per wavefront: gate + up tile)
+constexpr int kFeat2 = 128;       // FC2: output rows per unit (32 per wavefront: two tiles)
 constexpr int kU = 4;             // 128-wide K blocks per load group
 
 __device__ __forceinline__ float e4m3_prep(float v) {   // saturate to the e4m3 range
@@ -56,6 +58,7 @@ template <typename SRC>
 __global__ __launch_bounds__(256) void k_quant_rows(const SRC* __restrict__ src, int ncols, long long R,
                                                     const int32_t* __restrict__ src_row, uint8_t* __restrict__ q,
                                                     float* __restrict__ qs) {
+    constexpr int NIT = 8;                  // 4-block steps whose loads are issued together
     const int lane = threadIdx.x & 63;
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= R || src_row[row] < 0) return;
@@ -63,42 +66,52 @@ __global__ __launch_bounds__(256) void k_quant_rows(const SRC* __restrict__ src,
     const int g = lane >> 4, l16 = lane & 15;
     const SRC* s = src + (size_t)row * ncols;
     uint8_t* qr = q + (size_t)row * ncols;
-    for (int b0 = 0; b0 < nb; b0 += 4) {
-        const int b = b0 + g;
-        if (b < nb) {                       // whole 16-lane groups are active or not
-            float v[8];
+    for (int b0 = 0; b0 < nb; b0 += 4 * NIT) {
+        float v[NIT][8];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int b = b0 + 4 * it + g;
             const size_t c = (size_t)b * 128 + l16 * 8;
-            if constexpr (sizeof(SRC) == 2) {
-                const u32x4 w = *(const u32x4*)(s + c);
+            if (b < nb) {
+                if constexpr (sizeof(SRC) == 2) {
+                    const u32x4 w = *(const u32x4*)(s + c);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[2 * i] = bf16_lo(w[i]);
-                    v[2 * i + 1] = bf16_hi(w[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        v[it][2 * i] = bf16_lo(w[i]);
+                        v[it][2 * i + 1] = bf16_hi(w[i]);
+                    }
+                } else {
+                    const float4 a = *(const float4*)(s + c), bb = *(const float4*)(s + c + 4);
+                    v[it][0] = a.x; v[it][1] = a.y; v[it][2] = a.z; v[it][3] = a.w;
+                    v[it][4] = bb.x; v[it][5] = bb.y; v[it][6] = bb.z; v[it][7] = bb.w;
                 }
-            } else {
-                const float4 a = *(const float4*)(s + c), bb = *(const float4*)(s + c + 4);
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
             }
-            float amax = 0.f;
+        }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            amax = fmaxf(amax, __shfl_xor(amax, 4));
-            amax = fmaxf(amax, __shfl_xor(amax, 8));
-            const float sc = amax > 0.f ? amax / 448.f : 1.f;
-            uint2 out;
-            int p = 0;
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[0] / sc), e4m3_prep(v[1] / sc), p, false);
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[2] / sc), e4m3_prep(v[3] / sc), p, true);
-            out.x = (uint32_t)p;
-            p = 0;
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[4] / sc), e4m3_prep(v[5] / sc), p, false);
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[6] / sc), e4m3_prep(v[7] / sc), p, true);
-            out.y = (uint32_t)p;
-            *(uint2*)(qr + c) = out;
-            if (l16 == 0) qs[(size_t)row * nb + b] = sc;
+        for (int it = 0; it < NIT; ++it) {
+            const int b = b0 + 4 * it + g;
+            if (b < nb) {                   // whole 16-lane groups are active or not
+                const size_t c = (size_t)b * 128 + l16 * 8;
+                float amax = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[it][i]));
+                amax = fmaxf(amax, __shfl_xor(amax, 1));
+                amax = fmaxf(amax, __shfl_xor(amax, 2));
+                amax = fmaxf(amax, __shfl_xor(amax, 4));
+                amax = fmaxf(amax, __shfl_xor(amax, 8));
+                const float sc = amax > 0.f ? amax / 448.f : 1.f;
+                uint2 out;
+                int p = 0;
+                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][0] / sc), e4m3_prep(v[it][1] / sc), p, false);
+                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][2] / sc), e4m3_prep(v[it][3] / sc), p, true);
+                out.x = (uint32_t)p;
+                p = 0;
+                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][4] / sc), e4m3_prep(v[it][5] / sc), p, false);
+                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][6] / sc), e4m3_prep(v[it][7] / sc), p, true);
+                out.y = (uint32_t)p;
+                *(uint2*)(qr + c) = out;
+                if (l16 == 0) qs[(size_t)row * nb + b] = sc;
+            }
         }
     }
 }
@@ -118,13 +131,14 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
 }
 
 // One pass over up to 16*NTB rows (m0 .. m0+mv-1 of the segment) for this
-// wavefront's 16 features; NTB token blocks of 16 rows.
+// wavefront's two 16-row weight tiles (FC1: gate and up rows of 16 features;
+// FC2: 32 consecutive output rows); NTB token blocks of 16 rows.
 template <int MODE, int NTB>
 __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const float* __restrict__ Xs,
                                          const uint8_t* wg, const uint8_t* wu, const float* sg, const float* su,
                                          void* __restrict__ Outv, long long seg, int m0, int mv, int Kdim, int Nout,
                                          int f0, int lane) {
-    constexpr int U = MODE == 0 ? kU : 2 * kU;   // K blocks per group (FC2 loads half as much per block)
+    constexpr int U = kU;
     const int kq = (lane >> 4) * 16;
     const int nkb = Kdim / 128;
     f32x4 acc_g[NTB], acc_u[NTB];
@@ -146,9 +160,9 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
             a_g[u] = load_fp8x32(wg + (size_t)(kb0 + u) * 128);
-            if (MODE == 0) a_u[u] = load_fp8x32(wu + (size_t)(kb0 + u) * 128);
+            a_u[u] = load_fp8x32(wu + (size_t)(kb0 + u) * 128);
             s_g[u] = sg[kb0 + u];
-            s_u[u] = MODE == 0 ? su[kb0 + u] : 0.f;
+            s_u[u] = su[kb0 + u];
         }
 #pragma unroll
         for (int t = 0; t < NTB; ++t) {
@@ -159,11 +173,9 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
                 const f32x4 pg = mfma_fp8(a_g[u], bq);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc_g[t][i] = fmaf(pg[i], s_g[u] * sx, acc_g[t][i]);
-                if (MODE == 0) {
-                    const f32x4 pu = mfma_fp8(a_u[u], bq);
+                const f32x4 pu = mfma_fp8(a_u[u], bq);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc_u[t][i] = fmaf(pu[i], s_u[u] * sx, acc_u[t][i]);
-                }
+                for (int i = 0; i < 4; ++i) acc_u[t][i] = fmaf(pu[i], s_u[u] * sx, acc_u[t][i]);
             }
         }
     };
@@ -192,6 +204,9 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
             o.x = f32_to_bf16(acc_g[t][0]) | (f32_to_bf16(acc_g[t][1]) << 16);
             o.y = f32_to_bf16(acc_g[t][2]) | (f32_to_bf16(acc_g[t][3]) << 16);
             *(uint2*)((uint16_t*)Outv + orow) = o;
+            o.x = f32_to_bf16(acc_u[t][0]) | (f32_to_bf16(acc_u[t][1]) << 16);
+            o.y = f32_to_bf16(acc_u[t][2]) | (f32_to_bf16(acc_u[t][3]) << 16);
+            *(uint2*)((uint16_t*)Outv + orow + 16) = o;
         }
     }
 }
@@ -217,13 +232,15 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(const uint8_t* __restrict__ Xq
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = (lane >> 4) * 16;                  // this lane's 32 bytes inside a 128 block
     const int nkb = Kdim / 128;
-    const int f0 = unit * kFeat + wave * 16;          // first output feature of this wavefront
-    // weight rows of this lane: gate (and up) row f0 + lane%16
-    const int r_g = f0 + (lane & 15);
-    const uint8_t* wg = W + ((size_t)e * Wrows + r_g) * Kdim + kq;
-    const uint8_t* wu = W + ((size_t)e * Wrows + (MODE == 0 ? Nout + r_g : r_g)) * Kdim + kq;
-    const float* sg = Ws + ((size_t)e * (Wrows / 128) + f0 / 128) * nkb;
-    const float* su = Ws + ((size_t)e * (Wrows / 128) + (MODE == 0 ? (Nout + f0) / 128 : f0 / 128)) * nkb;
+    // first output feature (FC1) / output row (FC2) of this wavefront; its two
+    // weight tiles start at rows r0 and r1 (FC1: gate and up rows of features
+    // f0..f0+15; FC2: rows f0..f0+15 and f0+16..f0+31, one 128-row scale block)
+    const int f0 = MODE == 0 ? unit * kFeat + wave * 16 : unit * kFeat2 + wave * 32;
+    const int r0 = f0, r1 = MODE == 0 ? Nout + f0 : f0 + 16;
+    const uint8_t* wg = W + ((size_t)e * Wrows + r0 + (lane & 15)) * Kdim + kq;
+    const uint8_t* wu = W + ((size_t)e * Wrows + r1 + (lane & 15)) * Kdim + kq;
+    const float* sg = Ws + ((size_t)e * (Wrows / 128) + r0 / 128) * nkb;
+    const float* su = Ws + ((size_t)e * (Wrows / 128) + r1 / 128) * nkb;
 
     for (int m0 = 0; m0 < me; m0 += 16 * kMaxTB) {
         const int mv = min(16 * kMaxTB, me - m0);
@@ -268,7 +285,7 @@ hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in
                            h->seg_off, h->kept, R, d.H, 2 * F, F, upe);
     } else {
         hipLaunchKernelGGL(k_quant_rows<float>, dim3(qgrid), dim3(256), 0, s, act, F, R, h->src_row, aq, as);
-        const int upe = d.H / kFeat;
+        const int upe = d.H / kFeat2;
         hipLaunchKernelGGL(k_gemm_fp8<1>, dim3(d.E * upe), dim3(256), 0, s, aq, as, (const uint8_t*)w, ws, out,
                            h->seg_off, h->kept, R, F, d.H, d.H, upe);
     }

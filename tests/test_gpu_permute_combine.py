@@ -137,6 +137,51 @@ def test_permute_fp8_stress_full_size(fmt):
     assert np.array_equal(osc.cpu().numpy()[rows].view(np.uint32), wsc[rows].view(np.uint32))
 
 
+@pytest.mark.parametrize("T,H,E,K", [(5, 2056, 7, 3), (16, 7168, 256, 8), (33, 1000, 9, 4)])
+def test_combine_small_batch_column_slices(T, H, E, K):
+    """Few tokens: each row is cut into column slices over several wavefronts
+    (the last slice can be a single 16-byte chunk); weighted combine must
+    still match the oracle, and dispatch + identity combine must round-trip."""
+    r = np.random.default_rng(T * 31 + H)
+    idx = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int16)
+    lg = r.standard_normal((T, K))
+    pr = (np.exp(lg) / np.exp(lg).sum(axis=1, keepdims=True)).astype(np.float32)
+    log("combine small slices", T, H, E, K)
+    d = Dispatcher(T, H, E, K, pad_multiple=3)
+    d.preprocess(dev(idx), dev(pr))
+    Y = S.bf16_normal((d.R, H), T + 77)
+    y = d.combine(dev(Y))
+    x = S.bf16_normal((T, H), T + 78)
+    perm, *_ = d.dispatch(dev(x), dev(idx), dev(pr))
+    yi = d.combine(perm)
+    torch.cuda.synchronize()
+    rt = oracle.route(idx, 0, E, K, pr, 3, -1, d.R)
+    want = oracle.combine_bf16(Y, rt["row_id"], rt["copy_prob"])
+    g, w = S.bf16_to_float(host_bf16(y)), S.bf16_to_float(want)
+    assert row_rel_l2(g, w).max() < 1e-2
+    assert np.mean(host_bf16(y) == want) > 0.99
+    # probabilities sum to 1 and every copy survives: the weighted sum rounds back to x
+    assert np.array_equal(host_bf16(yi), x)
+
+
+@pytest.mark.parametrize("T,H,E,K", [(7, 1152, 6, 3), (1, 7168, 256, 8)])
+def test_permute_fp8_small_batch(T, H, E, K):
+    """fp8 rows with scales at batch sizes that split rows into slices."""
+    r = np.random.default_rng(T + 2 * H)
+    idx = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int16)
+    xq, xs = S.quantize_rows_fp8_torch(S.bf16_normal((T, H), T + 9))
+    log("permute fp8 small", T, H, E, K)
+    d = Dispatcher(T, H, E, K, payload="fp8", pad_multiple=4)
+    out, _, flag, _, osc = d.dispatch(dev(xq), dev(idx), x_scales=dev(xs))
+    torch.cuda.synchronize()
+    rt = oracle.route(idx, 0, E, K, None, 4, -1, d.R)
+    rows = _kept_rows(rt["src_row"])
+    assert np.array_equal(out.cpu().numpy()[rows], oracle.permute_rows(xq, rt["row_id"], d.R)[rows])
+    wsc = oracle.permute_rows(xs, rt["row_id"], d.R)
+    assert np.array_equal(osc.cpu().numpy()[rows].view(np.uint32), wsc[rows].view(np.uint32))
+    assert int(flag.item()) == 0
+
+
 def test_empty_batch():
     log("empty batch")
     d = Dispatcher(0, 256, 8, 2, pad_multiple=16)
