@@ -9,31 +9,38 @@
 // of expert e's segment: a = silu(W1g x) * (W1u x) stored bf16, then
 // y = W2 a stored bf16.
 //
-// Design (CDNA4, 256 CUs in 8 XCDs, 4 MB L2 per XCD):
-//  * Work unit = (expert, 128 weight rows).  For FC1 the 128 rows are 64 gate
-//    rows and the 64 matching up rows; for FC2 they are 128 output columns.
-//    A unit takes ALL of the expert's rows (in chunks of up to 320 tokens), so
-//    a weight row is streamed from HBM once per layer in the common case.
-//  * Experts are dealt to XCDs (expert e -> XCD e mod 8; hardware deals
-//    workgroups round-robin over XCDs, so workgroup b runs on XCD b mod 8).
-//    The 32 workgroups of an XCD walk that XCD's units in order, so at any
-//    time they share one expert: its token rows are read from L2, not HBM.
-//  * MFMA v_mfma_f32_32x32x16_bf16 with the weights as the A operand (rows of
-//    the 32x32 result = weight rows) and tokens as B (columns), so each lane
-//    ends up with 4 consecutive output features of one token: the epilogue
-//    stores 8 bytes per lane, and the FC1 gate/up values of a feature sit in
-//    the same lane for the SwiGLU.
-//  * Global -> LDS through global_load_lds_dwordx4 (no VGPR staging): token
-//    slices in a 2-deep ring (they come from L2), weight slices in a 4-deep
-//    ring (from HBM: ~48 KB in flight per CU).  The 16-byte chunk swizzle is
-//    applied on the global side so MFMA operand reads from LDS are bank
-//    conflict free (64 banks).  DMA instructions are interleaved one per MFMA.
-//  * 4 wavefronts; wave w owns token blocks w, w+4, w+8 (32 rows each) and
-//    all 4 weight blocks of the unit: per 16-wide K step 4 weight + up to 3
-//    token fragment reads feed up to 12 MFMAs; the next step's fragments load
-//    while the current step's MFMAs run, and the last step of a stage is
-//    deferred past the next barrier.  Token blocks past the expert's row
-//    count are neither loaded nor multiplied.
+// Design (CDNA4: 256 CUs in 8 XCDs, 4 MB L2 per XCD, 160 KB LDS per CU):
+//  * Work unit = (expert, 256 weight rows): for FC1 the gate and up rows of
+//    128 features, for FC2 256 output columns.  A unit takes all of the
+//    expert's token rows at once, so each weight row is streamed from HBM
+//    once per layer.  Segments of up to 256 rows take one 256-row pass;
+//    257..320 rows take two 128-row passes (the token chunk is then read
+//    twice, from L2); longer segments are cut into chunks of 320 rows.
+//  * Experts are dealt to XCDs (expert e -> XCD e mod 8; workgroup b runs on
+//    XCD b mod 8).  The 32 workgroups of an XCD walk that XCD's units in
+//    order and move through K at the same pace, so a token slice comes from
+//    HBM once and is then served by the XCD's L2.
+//  * 256-row pass: the four wavefronts form a 2x2 grid of 128 weight rows x
+//    up to 128 tokens each (256 accumulation registers).  Weight slices (HBM)
+//    are loaded with plain 16-byte loads into registers two 64-wide K stages
+//    ahead and copied into a 2-slot LDS ring; token slices (L2) go straight
+//    to LDS (global_load_lds_dwordx4) one stage ahead.  Measured on MI355X,
+//    this keeps more weight bandwidth next to the token stream than loading
+//    both through LDS-direct loads.  Each K step interleaves its MFMAs one by
+//    one with the next step's fragment reads and with one kind of side work
+//    (the copy into LDS, the token loads or the weight loads).
+//  * 128-row pass: four wavefronts each own all 4 weight blocks and token
+//    blocks w, w+4, w+8; both operands go global -> LDS directly (token ring
+//    2 deep, weight ring 4 deep), in the same LDS as the 256-row pass.
+//  * A 16-byte chunk swizzle keeps the LDS operand reads free of bank
+//    conflicts (64 banks).  MFMA v_mfma_f32_32x32x16_bf16 with weights as the
+//    A operand (rows of the 32x32 result = weight rows) and tokens as B
+//    (columns): each lane holds 4 consecutive features of one token, so the
+//    epilogue stores 8 bytes per lane and FC1's gate and up values of a
+//    feature sit in the same lane.  Every output element accumulates its K
+//    steps in ascending order in both passes.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -41,55 +48,70 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int NTOKB = 10;                        // token blocks (32 rows) per chunk
-constexpr int MCH = NTOKB * 32;                  // token rows per chunk (320)
-constexpr int TBW = (NTOKB + 3) / 4;             // most token blocks one wavefront owns (3)
-constexpr int NW = 128;                          // weight rows per unit
-constexpr int BK = 64;                           // K slice per stage
-constexpr int KS = BK / 16;                      // MFMA K steps per stage
-constexpr int CPR = BK / 8;                      // 16-byte chunks per row of a slice
-constexpr int X_CH = MCH * CPR;                  // chunks of a token stage
-constexpr int W_CH = NW * CPR;                   // chunks of a weight stage
-constexpr int X_LD = X_CH / 256;                 // token DMA instructions per wavefront per stage (10)
-constexpr int W_LD = W_CH / 256;                 // weight DMA instructions per wavefront per stage (4)
-constexpr int WAHEAD = 3;                        // weight stages in flight ahead of the computed one
-constexpr int NWSET = WAHEAD + 1;                // weight ring depth
+constexpr int BK = 64;                 // K per stage
+constexpr int KS = BK / 16;            // MFMA K steps per stage
+constexpr int CPR = BK / 8;            // 16-byte chunks per row of a stage
+constexpr int WROWS = 256;             // weight rows per unit
+constexpr int XROWS_A = 256;           // token rows of a 256-row pass
+constexpr int XROWS_B = 320;           // token rows of a chunk of 128-row passes
+constexpr int W_SLOT = WROWS * CPR;    // 16-byte chunks of a weight stage
+constexpr int X_SLOT = XROWS_B * CPR;  // 16-byte chunks of a token stage
 constexpr int kNxcd = 8;
-static_assert(X_CH % 256 == 0 && W_CH % 256 == 0, "whole DMA instructions");
-static_assert((2 * X_CH + NWSET * W_CH) * 16 + 8 * (kMaxE + 8) <= 160 * 1024, "LDS budget");
+static_assert((2 * W_SLOT + 2 * X_SLOT) * 16 + 8 * kMaxE + 64 <= 160 * 1024, "LDS budget");
 
-// Physical 16-byte slot of logical chunk `ch` of row `row` in a slice: the
-// XOR makes the 16 rows that one 16-lane group of an operand fetch touches
-// land on 16 distinct 16-byte bank groups of a 256-byte LDS line.
-__device__ __forceinline__ int swz(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
+// Physical 16-byte slot of logical chunk `ch` of row `row` in a stage (8
+// chunks per row, 2 rows per 256-byte LDS line): the XOR spreads the 16 rows
+// one 16-lane group of an operand fetch touches over 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row, int ch) { return row * CPR + (ch ^ ((row >> 1) & 7)); }
 
-// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4): lane
-// l's 16 bytes land at LDS address lds + 16*l.  Issued as inline asm so the
-// compiler does not treat every later LDS read as dependent on it (it would
-// otherwise drain all loads in flight before the first ds_read); completion
-// is awaited explicitly.  m0 is written only by these asm statements in this
-// translation unit, so the clobber of a reserved register is safe here.
+// Read one accumulator element where it lives (an accumulation register).
+// The explicit read keeps the compiler from copying every accumulator into
+// vector registers at once when the K loop ends.
+__device__ __forceinline__ float acc_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
+}
+
+typedef __attribute__((address_space(1))) const char gchar;   // global memory
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+
+// A global pointer value made explicitly wave-uniform (it is uniform by
+// construction); both halves stay unsigned, and the result keeps the global
+// address space so loads through it are global (not flat) loads.
+__device__ __forceinline__ gchar* uniform_ptr(const char* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (gchar*)(((uint64_t)hi << 32) | lo);
+}
+
+// One 16-byte-per-lane global -> LDS transfer (global_load_lds_dwordx4):
+// address = sbase (wave-uniform) + voff (per lane), lane l's 16 bytes land at
+// LDS byte address lds + 16*l.  Inline asm, so the compiler does not treat
+// later LDS reads as dependent on it; completion is awaited explicitly.  m0
+// is written only by these asm statements in this translation unit.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds) : "memory", "m0");
+__device__ __forceinline__ void dma16(gchar* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
-
-// LDS byte address of a __shared__ object (wave-uniform).
-__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)p);
-}
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// also drain the loads still in flight for later stages).
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (a fence would
+// also wait for the loads of later stages still in flight).  This wavefront's
+// LDS writes are complete before it arrives.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -98,7 +120,262 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-// K loop of one token chunk.
+// One pass: NWB weight blocks (32 rows) per wavefront over the workgroup's
+// 2*NWB weight blocks, NXB token blocks in the chunk, NTB of them (blocks
+// q, q+2, ...) owned by this wavefront.  All threads load; the MFMAs and the
+// epilogue belong to the wavefront.
+//   Weights: thread t loads row 32*b + t/8, 16-byte chunk t%8, of every
+//   weight block b into registers (per-lane offset `voff` plus a wave-uniform
+//   block base, wrow[b] = first row of block b) and writes it to LDS.
+//   Tokens: DMA instruction b of wavefront w fills LDS chunk slots
+//   256*b + 64*w + lane, i.e. row 32*b + 8*w + lane/8; `xoff`/`xoff_last`
+//   are the per-lane offsets (the last block's rows clamped to the chunk).
+template <int MODE, int NWB, int NXB, int NTB>
+__device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, const int (&wrow)[2 * NWB],
+                                     gchar* xbase, uint32_t voff, uint32_t xoff, uint32_t xoff_last, int pitch,
+                                     int nk, int lane, int wave, int p, int q, int mv, uint16_t* obase, int Nout,
+                                     int ocol0) {
+    constexpr int NWL = 2 * NWB;   // weight loads per thread per stage (one per block of 32 rows)
+    // LDS write slot of this thread's chunk within a block (same for every block)
+    const int tid = threadIdx.x;
+    const int wsl = (tid >> 3) * CPR + ((tid & 7) ^ (((tid >> 3) >> 1) & 7));
+    // operand fetch base of step s for rows (block*32 + lane%32)
+    int fb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int r = lane & 31, ch = 2 * s + (lane >> 5);
+        fb[s] = r * CPR + (ch ^ ((r >> 1) & 7));
+    }
+
+    f32x16 acc[NWB][NTB > 0 ? NTB : 1];
+#pragma unroll
+    for (int j = 0; j < NWB; ++j)
+#pragma unroll
+        for (int i = 0; i < (NTB > 0 ? NTB : 1); ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+
+    u32x4 sw0[NWL], sw1[NWL];
+    auto gload = [&](u32x4 (&sw)[NWL], int kt) {
+        // stages past the end re-read the last one (valid memory, L2 hits);
+        // keeps the number of loads in flight the same on every path
+        const int k = min(kt, nk - 1) * (BK * 2);
+#pragma unroll
+        for (int b = 0; b < NWL; ++b) sw[b] = *(const gu32x4*)(wbase + ((size_t)wrow[b] * pitch + k) + voff);
+    };
+    auto swrite = [&](const u32x4 (&sw)[NWL], int slot) {
+        u32x4* wl = wlds + slot * W_SLOT + wsl;
+#pragma unroll
+        for (int b = 0; b < NWL; ++b) wl[b * 32 * CPR] = sw[b];
+    };
+    const uint32_t xl0 = lds_addr_of(xlds) + wave * 64 * 16;
+    auto xdma = [&](int kt, int slot) {   // token stage kt -> LDS slot (NXB instructions per wavefront)
+        const int k = min(kt, nk - 1) * (BK * 2);
+#pragma unroll
+        for (int b = 0; b < NXB; ++b)
+            dma16(xbase + ((size_t)(b * 32) * pitch + k), b == NXB - 1 ? xoff_last : xoff,
+                  xl0 + (slot * X_SLOT + b * 256) * 16);
+    };
+    bf16x8 wf[2][NWB], xf[2][NTB > 0 ? NTB : 1];
+    auto frags = [&](int slot, int s, int buf) {
+        const u32x4* wl = wlds + slot * W_SLOT + fb[s] + p * NWB * 32 * CPR;
+        const u32x4* xl = xlds + slot * X_SLOT + fb[s] + q * 32 * CPR;
+#pragma unroll
+        for (int j = 0; j < NWB; ++j) wf[buf][j] = __builtin_bit_cast(bf16x8, wl[j * 32 * CPR]);
+#pragma unroll
+        for (int i = 0; i < NTB; ++i) xf[buf][i] = __builtin_bit_cast(bf16x8, xl[i * 64 * CPR]);
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NTB; ++i)
+#pragma unroll
+            for (int j = 0; j < NWB; ++j)
+                acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], xf[buf][i], acc[j][i], 0, 0, 0);
+    };
+    constexpr int NMF = NWB * (NTB > 0 ? NTB : 1);      // MFMAs per step
+    auto gload_h = [&](u32x4 (&sw)[NWL], int kt, int hh) {   // half hh of the refill loads
+        const int k = min(kt, nk - 1) * (BK * 2);
+#pragma unroll
+        for (int b = 0; b < NWL; ++b)
+            if (b % 2 == hh) sw[b] = *(const gu32x4*)(wbase + ((size_t)wrow[b] * pitch + k) + voff);
+    };
+    // One stage: 4 K steps of LDS slot `slot`; step s issues the fragment
+    // reads of step s+1 and one kind of side work, interleaved one by one with
+    // its MFMAs: step 0 the register -> LDS copy of weight stage kt+1, step 1
+    // the token DMA of stage kt+1, steps 2-3 the refill of the weight
+    // registers with stage kt+3.  Loads complete in issue order: the
+    // compiler's wait before the copy (it counts only its own loads, weight
+    // stage kt+2 after kt+1) finds stage kt+1 already landed and leaves stage
+    // kt+2 in flight; before the closing barrier token stage kt+1 must have
+    // landed, with only the NWL weight loads issued after it still in flight.
+    auto stage = [&](int slot, u32x4 (&sw)[NWL], int kt_x, int kt_load) {
+        if (NTB > 0) frags(slot, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        auto step = [&](auto stc) {
+            constexpr int st = decltype(stc)::value;
+            if (NTB > 0 && st + 1 < KS) frags(slot, st + 1, (st + 1) & 1);
+            if (NTB > 0) mfmas(st & 1);
+            if (st == 0) swrite(sw, slot ^ 1);
+            else if (st == 1) xdma(kt_x, slot ^ 1);
+            else gload_h(sw, kt_load, st - 2);
+            if (NTB > 0) {
+                constexpr int nside = st == 0 ? NWL : st == 1 ? 0 : NWL / 2;
+#pragma unroll
+                for (int i = 0; i < NMF; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, st);
+                    if (st + 1 < KS && i < NTB + NWB) __builtin_amdgcn_sched_group_barrier(0x100, 1, st);
+                    if (i < nside) __builtin_amdgcn_sched_group_barrier(st == 0 ? 0x200 : 0x020, 1, st);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+        static_assert(KS == 4, "four K steps per stage");
+        wait_vm<NWL>();
+        lds_barrier();
+    };
+
+    // prologue: token stage 0, weight stages 0 and 1 in flight; weight stage 0
+    // to slot 0; weight stage 2 in flight; token stage 0 and weight stage 0
+    // landed before the barrier (weight stages 1 and 2 may still fly).
+    xdma(0, 0);
+    gload(sw0, 0);
+    gload(sw1, 1);
+    swrite(sw0, 0);
+    gload(sw0, 2);
+    wait_vm<2 * NWL>();
+    lds_barrier();
+    // nk is even: each trip computes two stages from slots 0 and 1.
+    for (int kt = 0; kt < nk; kt += 2) {
+        stage(0, sw1, kt + 1, kt + 3);
+        stage(1, sw0, kt + 2, kt + 4);
+    }
+    wait_vm<0>();
+
+    // epilogue: lane holds token (lane&31) of each token block and weight rows
+    // 8*(r/4) + 4*(lane/32) + r%4 of each weight block
+    auto store_block = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < NTB) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int tok = (q + 2 * i) * 32 + (lane & 31);
+            if (tok < mv) {
+                uint16_t* orow = obase + (size_t)tok * Nout + ocol0 + (lane >> 5) * 4;
+                if (MODE == 0) {
+                    // gate blocks 0..NWB/2-1, up blocks NWB/2..NWB-1 (same features)
+#pragma unroll
+                    for (int j = 0; j < NWB / 2; ++j)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            float a[4];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float g = acc_read(acc[j][i][g4 * 4 + r]);
+                                const float u = acc_read(acc[j + NWB / 2][i][g4 * 4 + r]);
+                                a[r] = g / (1.f + __expf(-g)) * u;
+                            }
+                            uint2 v;
+                            v.x = pack_bf16x2(a[0], a[1]);
+                            v.y = pack_bf16x2(a[2], a[3]);
+                            *(uint2*)(orow + j * 32 + g4 * 8) = v;
+                        }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NWB; ++j)
+#pragma unroll
+                        for (int g4 = 0; g4 < 4; ++g4) {
+                            uint2 v;
+                            v.x = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 0]), acc_read(acc[j][i][g4 * 4 + 1]));
+                            v.y = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 2]), acc_read(acc[j][i][g4 * 4 + 3]));
+                            *(uint2*)(orow + j * 32 + g4 * 8) = v;
+                        }
+                }
+            }
+        }
+    };
+    store_block(std::integral_constant<int, 0>{});
+    store_block(std::integral_constant<int, 1>{});
+    store_block(std::integral_constant<int, 2>{});
+    store_block(std::integral_constant<int, 3>{});
+    store_block(std::integral_constant<int, 4>{});
+    static_assert(NTB <= 5, "one store_block call per token block");
+}
+
+// Weight-row offsets of the pass over features/columns [f0, f0 + 32*2*NWB/(MODE==0 ? 2 : 1))
+// and token-row offsets of the chunk, then the pass itself for this
+// wavefront's token-block count.
+template <int MODE, int NWB, int NXB>
+__device__ __forceinline__ void run_pass(u32x4* wlds, u32x4* xlds, const char* We, const char* Xc, int Kdim,
+                                         int Nout, int f0, int mv, uint16_t* ochunk, int lane, int p, int q) {
+    const int tid = threadIdx.x;
+    const int r8 = tid >> 3, c8 = (tid & 7) * 16;   // row within a 32-row block, byte offset of the chunk
+    // first weight row of each 32-row block of the pass (blocks never straddle
+    // the gate/up boundary, so rows inside a block are consecutive)
+    int wrow[2 * NWB];
+#pragma unroll
+    for (int b = 0; b < 2 * NWB; ++b) {
+        const int r = b * 32;
+        if (MODE == 0) {
+            // wavefront p: NWB/2 gate blocks then NWB/2 up blocks of features
+            // f0 + p*16*NWB .. +16*NWB-1
+            const int pp = r / (32 * NWB), rr = r % (32 * NWB), half = 16 * NWB;
+            wrow[b] = rr < half ? f0 + pp * half + rr : Nout + f0 + pp * half + rr - half;
+        } else {
+            wrow[b] = f0 + r;
+        }
+    }
+    const int pitch = Kdim * 2;
+    const uint32_t voff = (uint32_t)r8 * (uint32_t)pitch + (uint32_t)c8;
+    // token DMA lane: row 8*wave + lane/8 of a block, logical chunk of its swizzled slot
+    const int wave = tid >> 6, lane8 = (tid & 63) >> 3;
+    const int xr = 8 * wave + lane8;
+    const int xch = (tid & 7) ^ ((xr >> 1) & 7);
+    const uint32_t xoff = (uint32_t)xr * (uint32_t)pitch + (uint32_t)xch * 16u;
+    const uint32_t xoff_last = (uint32_t)min(xr, mv - 1 - (NXB - 1) * 32) * (uint32_t)pitch + (uint32_t)xch * 16u;
+    const int nk = Kdim / BK;
+    const int ocol0 = MODE == 0 ? f0 + p * 16 * NWB : f0 + p * 32 * NWB;
+    if (q == 0)
+        pass<MODE, NWB, NXB, (NXB + 1) / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff, xoff_last,
+                                            pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p, q, mv, ochunk,
+                                            Nout, ocol0);
+    else
+        pass<MODE, NWB, NXB, NXB / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff, xoff_last,
+                                      pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p, q, mv, ochunk, Nout,
+                                      ocol0);
+}
+
+// ---- 128-row passes (segments of 257..320 rows) ------------------------------
+// Work unit = (expert, 128 weight rows): FC1 64 gate + 64 up rows, FC2 128
+// output columns.  Four wavefronts, each owning all 4 weight blocks and token
+// blocks w, w+4, w+8 of a chunk of up to 320 rows.  Token slices come from L2
+// through a 2-deep LDS ring and weight slices from HBM through a 4-deep ring,
+// both by LDS-direct loads; the rings alias the LDS of the 256-row passes.
+constexpr int H_NTOKB = 10;                      // token blocks (32 rows) per chunk
+constexpr int H_MCH = H_NTOKB * 32;              // token rows per chunk (320)
+constexpr int TBW = (H_NTOKB + 3) / 4;           // most token blocks one wavefront owns (3)
+constexpr int H_NW = 128;                        // weight rows per pass
+constexpr int X_CH = H_MCH * CPR;                // chunks of a token stage
+constexpr int W_CH = H_NW * CPR;                 // chunks of a weight stage
+constexpr int X_LD = X_CH / 256;                 // token DMA instructions per wavefront per stage (10)
+constexpr int W_LD = W_CH / 256;                 // weight DMA instructions per wavefront per stage (4)
+constexpr int WAHEAD = 3;                        // weight stages in flight ahead of the computed one
+constexpr int NWSET = WAHEAD + 1;                // weight ring depth
+static_assert(2 * X_CH == 2 * X_SLOT && NWSET * W_CH == 2 * W_SLOT, "128-row rings alias the 256-row slots");
+
+// One 16-byte-per-lane global -> LDS transfer from a per-lane 64-bit address.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16v(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+typedef __bf16 bf16x8h __attribute__((ext_vector_type(8)));
+
+// K loop of a 128-row pass over one token chunk.
 //  * Token slices go through a 2-deep LDS ring (stage kt+1 is loaded while kt
 //    is computed; they come from L2), weight slices through a (WAHEAD+1)-deep
 //    ring (they come from HBM and need more bytes in flight).
@@ -120,10 +397,10 @@ __device__ __forceinline__ void mainloop(u32x4* xring, u32x4* wring, const uint1
     const uint32_t xl0 = lds_addr_of(xring) + wave * 64 * 16;
     const uint32_t wl0 = lds_addr_of(wring) + wave * 64 * 16;
     auto dma_x = [&](int kt, int q) {   // token DMA q of stage kt (rows of block q)
-        if (q < nblk) dma16(xbase + xofs[q] + kt * BK, xl0 + ((kt & 1) * X_CH + q * 256) * 16);
+        if (q < nblk) dma16v(xbase + xofs[q] + kt * BK, xl0 + ((kt & 1) * X_CH + q * 256) * 16);
     };
     auto dma_w = [&](int kt, int q) {
-        dma16(wbase + wofs[q] + kt * BK, wl0 + ((kt % NWSET) * W_CH + q * 256) * 16);
+        dma16v(wbase + wofs[q] + kt * BK, wl0 + ((kt % NWSET) * W_CH + q * 256) * 16);
     };
     int woff[KS][4], xoff[KS][TBW];
 #pragma unroll
@@ -217,57 +494,14 @@ __device__ __forceinline__ void mainloop(u32x4* xring, u32x4* wring, const uint1
     lds_barrier();   // the rings are free before the next chunk / unit refills them
 }
 
-template <int MODE>  // 0: FC1 + SwiGLU (out = act [R,F]); 1: FC2 (out = expert_out [R,H])
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Out,
-    const int64_t* __restrict__ seg_off, const int32_t* __restrict__ kept, int E, long long R, int Kdim,
-    int Wrows, int Nout, int n_units) {
-    __shared__ u32x4 xring[2 * X_CH];
-    __shared__ u32x4 wring[NWSET * W_CH];
-    __shared__ int s_list[kMaxE];      // active experts of this XCD, ascending
-    __shared__ int s_rows[kMaxE];      // their row counts (clipped to R)
-    __shared__ int s_cnt;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = gridDim.x, b = blockIdx.x;
-    const int nx = (G % kNxcd == 0) ? kNxcd : 1;
-    const int xcd = b % nx, P = G / nx, j = b / nx;
-
-    // ---- this XCD's experts that have rows (wavefront 0, ballot compaction) --
-    if (wave == 0) {
-        int run = 0;
-        for (int c = 0; c * nx < E; c += 64) {
-            const int e = xcd + nx * (c + lane);
-            int m = 0;
-            if (e < E) {
-                const long long so = seg_off[e];
-                long long mm = so < R ? (long long)kept[e] : 0;
-                if (so + mm > R) mm = R - so;
-                m = (int)mm;
-            }
-            const unsigned long long act = __ballot(m > 0);
-            if (m > 0) {
-                const int pos = run + __popcll(act & ((1ull << lane) - 1ull));
-                s_list[pos] = e;
-                s_rows[pos] = m;
-            }
-            run += __popcll(act);
-        }
-        if (lane == 0) s_cnt = run;
-    }
-    __syncthreads();
-    const int total = s_cnt * n_units;
-
-    for (int t = j; t < total; t += P) {
-        const int slot = t / n_units, nt = t - slot * n_units;
-        const int e = s_list[slot];
-        const int me = s_rows[slot];
-        const long long seg = seg_off[e];
-        const uint16_t* Wb = W + (size_t)e * Wrows * Kdim;
-        const int n0 = (MODE == 0) ? nt * 64 : nt * 128;
-
-        // weight DMA q of wavefront w fills slots (q*4+w)*64.. of a stage:
+// One 128-row pass of unit rows: weights from We (expert base), features
+// (FC1) / columns (FC2) starting at n0, over a chunk of me_c rows starting at
+// token row X (segment row m0 = 0 of the chunk), output rows Out.
+template <int MODE>
+__device__ __forceinline__ void half_pass(u32x4* xring, u32x4* wring, const uint16_t* X, const uint16_t* Wb,
+                                          uint16_t* Out, long long seg, int me, int Kdim, int Nout, int n0,
+                                          int wave, int lane) {
+    // weight DMA q of wavefront w fills slots (q*4+w)*64.. of a stage:
         // rows 8*(q*4+w)..+7, each lane the logical chunk of its slot
         int wofs[W_LD];
 #pragma unroll
@@ -279,8 +513,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             wofs[q] = wr * Kdim + ch * 8;
         }
 
-        for (int m0 = 0; m0 < me; m0 += MCH) {
-            const int mv = min(MCH, me - m0);
+        for (int m0 = 0; m0 < me; m0 += H_MCH) {
+            const int mv = min(H_MCH, me - m0);
             const int nblk = (mv + 31) / 32;                // token blocks holding rows
             const uint16_t* Xb = X + (size_t)(seg + m0) * Kdim;
             // token DMA q covers rows 32q + 8*wave .. +7 (block q)
@@ -315,6 +549,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             // weight rows 8*(r/4) + 4*(lane/32) + r%4 of each weight block.
 #pragma unroll
             for (int i = 0; i < TBW; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
                 const int tok = (wave + 4 * i) * 32 + (lane & 31);
                 if (i >= ntb || tok >= mv) continue;
                 uint16_t* orow = Out + (size_t)(seg + m0 + tok) * Nout + n0;
@@ -326,7 +561,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                             float a[4];
 #pragma unroll
                             for (int q = 0; q < 4; ++q) {
-                                const float g = acc[nb][i][g4 * 4 + q], u = acc[nb + 2][i][g4 * 4 + q];
+                                const float g = acc_read(acc[nb][i][g4 * 4 + q]), u = acc_read(acc[nb + 2][i][g4 * 4 + q]);
                                 a[q] = g / (1.f + __expf(-g)) * u;
                             }
                             uint2 v;
@@ -340,11 +575,86 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
                         for (int g4 = 0; g4 < 4; ++g4) {
                             uint2 v;
-                            v.x = pack_bf16x2(acc[nb][i][g4 * 4 + 0], acc[nb][i][g4 * 4 + 1]);
-                            v.y = pack_bf16x2(acc[nb][i][g4 * 4 + 2], acc[nb][i][g4 * 4 + 3]);
+                            v.x = pack_bf16x2(acc_read(acc[nb][i][g4 * 4 + 0]), acc_read(acc[nb][i][g4 * 4 + 1]));
+                            v.y = pack_bf16x2(acc_read(acc[nb][i][g4 * 4 + 2]), acc_read(acc[nb][i][g4 * 4 + 3]));
                             *(uint2*)(orow + nb * 32 + g4 * 8 + (lane >> 5) * 4) = v;
                         }
                 }
+            }
+        }
+}
+
+template <int MODE>  // 0: FC1 + SwiGLU (out = act [R,F]); 1: FC2 (out = expert_out [R,H])
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Out,
+    const int64_t* __restrict__ seg_off, const int32_t* __restrict__ kept, int E, long long R, int Kdim,
+    int Wrows, int Nout, int n_units) {
+    __shared__ u32x4 wlds[2 * W_SLOT];
+    __shared__ u32x4 xlds[2 * X_SLOT];
+    __shared__ int s_list[kMaxE];      // active experts of this XCD, ascending
+    __shared__ int s_rows[kMaxE];      // their row counts (clipped to R)
+    __shared__ int s_cnt;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p = wave >> 1, q = wave & 1;
+    const int G = gridDim.x, b = blockIdx.x;
+    const int nxcd = (G % kNxcd == 0) ? kNxcd : 1;
+    const int xcd = b % nxcd, P = G / nxcd, j = b / nxcd;
+
+    // ---- this XCD's experts that have rows (wavefront 0, ballot compaction) --
+    if (wave == 0) {
+        int run = 0;
+        for (int c = 0; c * nxcd < E; c += 64) {
+            const int e = xcd + nxcd * (c + lane);
+            int m = 0;
+            if (e < E) {
+                const long long so = seg_off[e];
+                long long mm = so < R ? (long long)kept[e] : 0;
+                if (so + mm > R) mm = R - so;
+                m = (int)mm;
+            }
+            const unsigned long long act = __ballot(m > 0);
+            if (m > 0) {
+                const int pos = run + __popcll(act & ((1ull << lane) - 1ull));
+                s_list[pos] = e;
+                s_rows[pos] = m;
+            }
+            run += __popcll(act);
+        }
+        if (lane == 0) s_cnt = run;
+    }
+    __syncthreads();
+    const int total = s_cnt * n_units;
+
+    for (int t = j; t < total; t += P) {
+        const int slot = t / n_units, nt = t - slot * n_units;
+        const int e = s_list[slot];
+        const int me = s_rows[slot];
+        const long long seg = seg_off[e];
+        const char* We = (const char*)(W + (size_t)e * Wrows * Kdim);
+        const int u0 = nt * (MODE == 0 ? 128 : 256);    // first feature (FC1) / output column (FC2) of the unit
+
+        for (int m0 = 0; m0 < me; ) {
+            const int left = me - m0;
+            const char* Xc = (const char*)(X + (size_t)(seg + m0) * Kdim);
+            uint16_t* oc = Out + (size_t)(seg + m0) * Nout;
+            if (left <= XROWS_A) {
+                const int mv = left, nblk = (mv + 31) / 32;
+                switch (nblk) {
+#define MOE_A(NB) case NB: run_pass<MODE, 4, NB>(wlds, xlds, We, Xc, Kdim, Nout, u0, mv, oc, lane, p, q); break;
+                    MOE_A(1) MOE_A(2) MOE_A(3) MOE_A(4) MOE_A(5) MOE_A(6) MOE_A(7) default: MOE_A(8)
+#undef MOE_A
+                }
+                m0 += mv;
+            } else {
+                // 257..320 rows: two 128-row passes with the token chunk in L2
+                const int mv = min(left, XROWS_B);
+                const uint16_t* Wb = W + (size_t)e * Wrows * Kdim;
+                for (int h = 0; h < 2; ++h)
+                    half_pass<MODE>(xlds, wlds, X, Wb, Out, seg + m0, mv, Kdim, Nout,
+                                    u0 + h * (MODE == 0 ? 64 : 128), wave, lane);
+                m0 += mv;
             }
         }
     }
@@ -361,10 +671,10 @@ hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* i
     if (grid < kNxcd) grid = num_cu;
     if (stage == 0) {
         hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(grid), dim3(256), 0, s, (const uint16_t*)in, (const uint16_t*)w,
-                           (uint16_t*)out, h->seg_off, h->kept, d.E, R, d.H, 2 * F, F, F / 64);
+                           (uint16_t*)out, h->seg_off, h->kept, d.E, R, d.H, 2 * F, F, F / 128);
     } else {
         hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(grid), dim3(256), 0, s, (const uint16_t*)in, (const uint16_t*)w,
-                           (uint16_t*)out, h->seg_off, h->kept, d.E, R, F, d.H, d.H, d.H / 128);
+                           (uint16_t*)out, h->seg_off, h->kept, d.E, R, F, d.H, d.H, d.H / 256);
     }
     return hipGetLastError();
 }
