@@ -63,6 +63,9 @@ def main() -> int:
                     help="also time the permute/combine, fp8 routing-stress and decode workloads and a plain copy")
     ap.add_argument("--calib-copy", action="store_true",
                     help="end with one 1 GiB device copy (reference dispatch for hardware byte counters)")
+    ap.add_argument("--workload", choices=("dsv3_layer", "decode"), default="dsv3_layer",
+                    help="decode: only the fp8 decode layer, eager, for kernel profiling")
+    ap.add_argument("--tokens", type=int, default=16, help="decode workload: live tokens (bucket = next pow2)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -80,6 +83,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = "cuda"
+    if args.workload == "decode":
+        return run_decode(args)
     c = S.CONFIGS["cfg4_dsv3_layer"]
     T, H, E, K, F, pad = c.T, c.H, c.E, c.K, c.F, c.pad
 
@@ -306,6 +311,50 @@ def _event_times(fn, reps=30, warm=5):
         b.synchronize()
         t.append(a.elapsed_time(b))
     return min(t), st.median(t)
+
+
+def run_decode(args):
+    """Decode-sized layer with fp8 weights, eager launches: routing metadata,
+    permute, FC1 + SwiGLU, FC2, combine for `--tokens` live tokens in the
+    next power-of-two bucket.  One JSON line (milliseconds per layer)."""
+    import numpy as np
+    import torch
+
+    import moe_synth as S
+    from combine_routing_preprocess_amd import Dispatcher
+    dev = "cuda"
+    c = S.CONFIGS["cfg5_decode_fp8"]
+    T_live = args.tokens
+    T = S.next_pow2_bucket(T_live)
+    log(f"drawing fp8 weights; {T_live} live tokens in bucket {T}")
+    w1q, w1s = S.weights_fp8_blocks(c.E, 2 * c.F, c.H, c.seed + 1, device=dev)
+    w2q, w2s = S.weights_fp8_blocks(c.E, c.H, c.F, c.seed + 2, device=dev)
+    idx, pr = S.route_sigmoid_topk(T, c.E, c.K, c.seed + T)
+    x = torch.from_numpy(S.bf16_normal((T, c.H), c.seed + T).view(np.int16)).to(dev).view(torch.bfloat16)
+    d = Dispatcher(T, c.H, c.E, c.K, pad_multiple=c.pad)
+    rt, pt = torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev)
+    tl = torch.tensor([T_live], dtype=torch.int32, device=dev)
+    perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+    scr = d.alloc_mlp_scratch(c.F, "fp8")
+    eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, scratch=scr, expert_out=eo, out=y,
+                T_live=tl)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(json.dumps({"workload": f"decode_fp8: {T_live} live tokens (bucket {T}) x {c.H}, {c.E} experts top-{c.K}, "
+                                  f"FFN {c.F}, fp8 e4m3 weights", "ms_per_layer_eager": round(ms, 4),
+                      "steps": args.steps}), flush=True)
+    return 0
 
 
 def run_extra(args):

@@ -52,66 +52,70 @@ __device__ __forceinline__ float e4m3_prep(float v) {   // saturate to the e4m3 
 // ---- row quantiser ------------------------------------------------------------
 // Rows r with src_row[r] >= 0 (rows that hold a kept copy): src [R, ncols]
 // (bf16 bit patterns or fp32) -> q [R, ncols] e4m3 codes, qs [R, ncols/128]
-// scales.  One wavefront per row; 16 lanes per 128-column block, 8 values
-// per lane, 4 blocks per step.
+// scales.  One wavefront per (row, group of 8 column blocks of 128); 16
+// lanes per block, 8 values per lane, 4 blocks per step, the loads of both
+// steps issued together.
+constexpr int kQBlocks = 8;                  // 128-column blocks per wavefront
+
 template <typename SRC>
 __global__ __launch_bounds__(256) void k_quant_rows(const SRC* __restrict__ src, int ncols, long long R,
                                                     const int32_t* __restrict__ src_row, uint8_t* __restrict__ q,
                                                     float* __restrict__ qs) {
-    constexpr int NIT = 8;                  // 4-block steps whose loads are issued together
+    constexpr int NIT = kQBlocks / 4;
     const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= R || src_row[row] < 0) return;
     const int nb = ncols / 128;
+    const int ngrp = (nb + kQBlocks - 1) / kQBlocks;
+    const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long row = wv / ngrp;
+    if (row >= R || src_row[row] < 0) return;
+    const int b0 = (int)(wv - row * ngrp) * kQBlocks;
     const int g = lane >> 4, l16 = lane & 15;
     const SRC* s = src + (size_t)row * ncols;
     uint8_t* qr = q + (size_t)row * ncols;
-    for (int b0 = 0; b0 < nb; b0 += 4 * NIT) {
-        float v[NIT][8];
+    float v[NIT][8];
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int b = b0 + 4 * it + g;
-            const size_t c = (size_t)b * 128 + l16 * 8;
-            if (b < nb) {
-                if constexpr (sizeof(SRC) == 2) {
-                    const u32x4 w = *(const u32x4*)(s + c);
+    for (int it = 0; it < NIT; ++it) {
+        const int b = b0 + 4 * it + g;
+        const size_t c = (size_t)b * 128 + l16 * 8;
+        if (b < nb) {
+            if constexpr (sizeof(SRC) == 2) {
+                const u32x4 w = *(const u32x4*)(s + c);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        v[it][2 * i] = bf16_lo(w[i]);
-                        v[it][2 * i + 1] = bf16_hi(w[i]);
-                    }
-                } else {
-                    const float4 a = *(const float4*)(s + c), bb = *(const float4*)(s + c + 4);
-                    v[it][0] = a.x; v[it][1] = a.y; v[it][2] = a.z; v[it][3] = a.w;
-                    v[it][4] = bb.x; v[it][5] = bb.y; v[it][6] = bb.z; v[it][7] = bb.w;
+                for (int i = 0; i < 4; ++i) {
+                    v[it][2 * i] = bf16_lo(w[i]);
+                    v[it][2 * i + 1] = bf16_hi(w[i]);
                 }
+            } else {
+                const float4 a = *(const float4*)(s + c), bb = *(const float4*)(s + c + 4);
+                v[it][0] = a.x; v[it][1] = a.y; v[it][2] = a.z; v[it][3] = a.w;
+                v[it][4] = bb.x; v[it][5] = bb.y; v[it][6] = bb.z; v[it][7] = bb.w;
             }
         }
+    }
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int b = b0 + 4 * it + g;
-            if (b < nb) {                   // whole 16-lane groups are active or not
-                const size_t c = (size_t)b * 128 + l16 * 8;
-                float amax = 0.f;
+    for (int it = 0; it < NIT; ++it) {
+        const int b = b0 + 4 * it + g;
+        if (b < nb) {                       // whole 16-lane groups are active or not
+            const size_t c = (size_t)b * 128 + l16 * 8;
+            float amax = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[it][i]));
-                amax = fmaxf(amax, __shfl_xor(amax, 1));
-                amax = fmaxf(amax, __shfl_xor(amax, 2));
-                amax = fmaxf(amax, __shfl_xor(amax, 4));
-                amax = fmaxf(amax, __shfl_xor(amax, 8));
-                const float sc = amax > 0.f ? amax / 448.f : 1.f;
-                uint2 out;
-                int p = 0;
-                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][0] / sc), e4m3_prep(v[it][1] / sc), p, false);
-                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][2] / sc), e4m3_prep(v[it][3] / sc), p, true);
-                out.x = (uint32_t)p;
-                p = 0;
-                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][4] / sc), e4m3_prep(v[it][5] / sc), p, false);
-                p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][6] / sc), e4m3_prep(v[it][7] / sc), p, true);
-                out.y = (uint32_t)p;
-                *(uint2*)(qr + c) = out;
-                if (l16 == 0) qs[(size_t)row * nb + b] = sc;
-            }
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[it][i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            amax = fmaxf(amax, __shfl_xor(amax, 4));
+            amax = fmaxf(amax, __shfl_xor(amax, 8));
+            const float sc = amax > 0.f ? amax / 448.f : 1.f;
+            uint2 out;
+            int p = 0;
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][0] / sc), e4m3_prep(v[it][1] / sc), p, false);
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][2] / sc), e4m3_prep(v[it][3] / sc), p, true);
+            out.x = (uint32_t)p;
+            p = 0;
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][4] / sc), e4m3_prep(v[it][5] / sc), p, false);
+            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][6] / sc), e4m3_prep(v[it][7] / sc), p, true);
+            out.y = (uint32_t)p;
+            *(uint2*)(qr + c) = out;
+            if (l16 == 0) qs[(size_t)row * nb + b] = sc;
         }
     }
 }
@@ -276,15 +280,18 @@ hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in
     float* xs = (float*)((char*)xq + up256((size_t)R * d.H));
     uint8_t* aq = (uint8_t*)((char*)xs + up256((size_t)R * (d.H / 128) * 4));
     float* as = (float*)((char*)aq + up256((size_t)R * F));
-    const int qgrid = (int)((R + 3) / 4);
+    auto qgrid = [&](int ncols) {   // (row, block group) wavefronts, four per workgroup
+        const long long ngrp = (ncols / 128 + kQBlocks - 1) / kQBlocks;
+        return (unsigned)((R * ngrp + 3) / 4);
+    };
     if (stage == 0) {
-        hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(qgrid), dim3(256), 0, s, (const uint16_t*)in, d.H, R,
+        hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(qgrid(d.H)), dim3(256), 0, s, (const uint16_t*)in, d.H, R,
                            h->src_row, xq, xs);
         const int upe = F / kFeat;
         hipLaunchKernelGGL(k_gemm_fp8<0>, dim3(d.E * upe), dim3(256), 0, s, xq, xs, (const uint8_t*)w, ws, act,
                            h->seg_off, h->kept, R, d.H, 2 * F, F, upe);
     } else {
-        hipLaunchKernelGGL(k_quant_rows<float>, dim3(qgrid), dim3(256), 0, s, act, F, R, h->src_row, aq, as);
+        hipLaunchKernelGGL(k_quant_rows<float>, dim3(qgrid(F)), dim3(256), 0, s, act, F, R, h->src_row, aq, as);
         const int upe = d.H / kFeat2;
         hipLaunchKernelGGL(k_gemm_fp8<1>, dim3(d.E * upe), dim3(256), 0, s, aq, as, (const uint8_t*)w, ws, out,
                            h->seg_off, h->kept, R, F, d.H, d.H, upe);
