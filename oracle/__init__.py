@@ -74,6 +74,10 @@ def lib():
         L.orc_quant_rows_e4m3_f32.argtypes = [C.c_int32, C.c_int32, P, P, P]
         L.orc_expert_mlp_fp8.restype = None
         L.orc_expert_mlp_fp8.argtypes = [C.c_int32, C.c_int32, C.c_int32] + [P] * 6
+        L.orc_dispatch_backward.restype = None
+        L.orc_dispatch_backward.argtypes = [C.c_int32] * 5 + [P] * 6
+        L.orc_combine_backward.restype = None
+        L.orc_combine_backward.argtypes = [C.c_int32] * 5 + [P] * 3 + [C.c_int32] + [P] * 4
         L.orc_set_threads.restype = None
         L.orc_set_threads.argtypes = [C.c_int]
         L.orc_get_threads.restype = C.c_int
@@ -191,6 +195,41 @@ def combine_bf16(Y: np.ndarray, row_id: np.ndarray, copy_prob: np.ndarray, apply
         lib().orc_combine_bf16(T, K, H, _p(_c(row_id, np.int32)), _p(_c(copy_prob, np.float32)),
                                1 if apply_probs else 0, _p(Y), _p(y))
     return y
+
+
+def dispatch_backward(grad_out: np.ndarray, rt: dict, E: int, sparse: bool, grad_out_probs=None):
+    """Gradients of a dispatch: (grad_x [T,H] bf16 bits, grad_probs or None).
+    grad_probs has the routing's shape ([T,K] dense, [T,E] sparse)."""
+    rid = _c(rt["row_id"], np.int32)
+    T, K = rid.shape
+    grad_out = _c(grad_out, np.uint16)
+    H = grad_out.shape[1]
+    gx = np.zeros((T, H), np.uint16)
+    gop = None if grad_out_probs is None else _c(grad_out_probs, np.float32)
+    gp = None if gop is None else np.zeros((T, E if sparse else K), np.float32)
+    if T:
+        lib().orc_dispatch_backward(T, K, E, H, 1 if sparse else 0, _p(rid), _p(_c(rt["copy_expert"], np.int32)),
+                                    _p(grad_out), _p(gop), _p(gx), _p(gp))
+    return gx, gp
+
+
+def combine_backward(grad_y: np.ndarray, Y: np.ndarray, rt: dict, E: int, sparse: bool,
+                     apply_probs: bool = True, want_probs: bool = True, fill: int = 0):
+    """Gradients of a combine: (grad_Y [R,H] bf16 bits, rows holding no kept
+    copy keep ``fill``; grad_probs in the routing's shape, or None)."""
+    rid = _c(rt["row_id"], np.int32)
+    T, K = rid.shape
+    grad_y = _c(grad_y, np.uint16)
+    Y = _c(Y, np.uint16)
+    H = grad_y.shape[1]
+    R = Y.shape[0]
+    gY = np.full((R, H), fill, np.uint16)
+    gp = np.zeros((T, E if sparse else K), np.float32) if want_probs else None
+    if T:
+        lib().orc_combine_backward(T, K, E, H, 1 if sparse else 0, _p(rid), _p(_c(rt["copy_expert"], np.int32)),
+                                   _p(_c(rt["copy_prob"], np.float32)), 1 if apply_probs else 0,
+                                   _p(grad_y), _p(Y), _p(gY), _p(gp))
+    return gY, gp
 
 
 def expert_mlp_bf16(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, return_a: bool = False):

@@ -323,6 +323,83 @@ void orc_combine_bf16(int32_t T, int32_t K, int32_t H, const int32_t* row_id,
 }
 
 /* ------------------------------------------------------------------------ */
+/* backward of dispatch                                                      */
+/* [P2] "Full HybridEP reference validation": hidden-state and probability    */
+/* gradients of the backward-of-dispatch communication.  Dispatch copies      */
+/* token t's row (and the copy's probability) to row row_id[t,j] for every    */
+/* kept copy, so the gradient of token t is the sum of its kept copies' row   */
+/* gradients (double, one rounding to bf16; 0 with no kept copy), and the     */
+/* gradient of probability (t, j) is the probability gradient of its row.     */
+/* grad_probs has the routing's shape: dense [T,K] by slot, sparse [T,E] by   */
+/* expert (copy_expert), 0 wherever no copy was kept.                         */
+/* ------------------------------------------------------------------------ */
+void orc_dispatch_backward(int32_t T, int32_t K, int32_t E, int32_t H, int32_t sparse,
+                           const int32_t* row_id, const int32_t* copy_expert,
+                           const uint16_t* grad_out, const float* grad_out_probs,
+                           uint16_t* grad_x, float* grad_probs) {
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t h = 0; h < H; h++) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < K; j++) {
+                int32_t r = row_id[(int64_t)t * K + j];
+                if (r >= 0) acc += orc_bf16_to_double(grad_out[(int64_t)r * H + h]);
+            }
+            grad_x[(int64_t)t * H + h] = orc_bf16_from_double(acc);
+        }
+    }
+    if (!grad_probs || !grad_out_probs) return;
+    const int64_t width = sparse ? E : K;
+    for (int64_t i = 0; i < (int64_t)T * width; i++) grad_probs[i] = 0.0f;
+    for (int32_t t = 0; t < T; t++)
+        for (int32_t j = 0; j < K; j++) {
+            int32_t r = row_id[(int64_t)t * K + j];
+            if (r < 0) continue;
+            int64_t col = sparse ? copy_expert[(int64_t)t * K + j] : j;
+            grad_probs[(int64_t)t * width + col] = grad_out_probs[r];
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* backward of combine                                                       */
+/* [P2] "Full HybridEP reference validation": hidden-state and probability    */
+/* gradients of the backward-of-combine communication.  With                  */
+/* y[t] = sum_j w_tj * Y[row_id[t,j]], w = the copy probability when          */
+/* probabilities are applied, else 1:                                         */
+/*   dL/dY[row_id[t,j]] = w_tj * dL/dy[t]  (product in double, one rounding   */
+/*   to bf16; rows holding no kept copy are not written), and                 */
+/*   dL/dp_tj = sum_h dL/dy[t,h] * Y[row_id[t,j],h]  (double, then float)     */
+/*   when probabilities are applied, 0 otherwise and for dropped copies.      */
+/* grad_probs has the routing's shape as in the dispatch backward.            */
+/* ------------------------------------------------------------------------ */
+void orc_combine_backward(int32_t T, int32_t K, int32_t E, int32_t H, int32_t sparse,
+                          const int32_t* row_id, const int32_t* copy_expert,
+                          const float* copy_prob, int32_t apply_probs, const uint16_t* grad_y,
+                          const uint16_t* Y, uint16_t* grad_Y, float* grad_probs) {
+    const int64_t width = sparse ? E : K;
+    if (grad_probs)
+        for (int64_t i = 0; i < (int64_t)T * width; i++) grad_probs[i] = 0.0f;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t j = 0; j < K; j++) {
+            int32_t r = row_id[(int64_t)t * K + j];
+            if (r < 0) continue;
+            double w = apply_probs ? (double)copy_prob[(int64_t)t * K + j] : 1.0;
+            double dot = 0.0;
+            for (int32_t h = 0; h < H; h++) {
+                double g = orc_bf16_to_double(grad_y[(int64_t)t * H + h]);
+                grad_Y[(int64_t)r * H + h] = orc_bf16_from_double(w * g);
+                if (grad_probs && apply_probs) dot += g * orc_bf16_to_double(Y[(int64_t)r * H + h]);
+            }
+            if (grad_probs) {
+                int64_t col = sparse ? copy_expert[(int64_t)t * K + j] : j;
+                grad_probs[(int64_t)t * width + col] = apply_probs ? (float)dot : 0.0f;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* expert MLP (bf16 weights)                                                 */
 /* [P1] "Summary"/"Configuration": a grouped FC1 -> activation -> FC2 MLP     */
 /* writing FC2 into a caller-owned buffer; [P5] streaming-load commit: FC1    */
