@@ -261,6 +261,63 @@ class Dispatcher:
                                     _stream()), "moe_combine")
         return out
 
+    # ---- backward ---------------------------------------------------------------
+    def _probs_grad_shape(self):
+        return (self.T, self.E) if self.route_fmt == A.ROUTE_SPARSE_BOOL else (self.T, self.K)
+
+    def _grad_probs_out(self, grad_probs):
+        if grad_probs is None:
+            grad_probs = torch.empty(self._probs_grad_shape(), dtype=torch.float32, device=self.device)
+        self._dev(grad_probs, "grad_probs")
+        _need(grad_probs.dtype == torch.float32 and tuple(grad_probs.shape) == self._probs_grad_shape(),
+              "grad_probs must be float32 in the routing's shape")
+        return grad_probs
+
+    def dispatch_backward(self, grad_out: torch.Tensor, grad_out_probs: Optional[torch.Tensor] = None, *,
+                          out: Optional[torch.Tensor] = None, grad_probs: Optional[torch.Tensor] = None):
+        """Gradients of a dispatch: (grad_x [T,H] bf16, grad_probs or None).
+        grad_probs (routing-shaped fp32) is produced when grad_out_probs [R]
+        is given."""
+        self._dev(grad_out, "grad_out")
+        _need(grad_out.dtype == torch.bfloat16 and tuple(grad_out.shape) == (self.R, self.H),
+              "grad_out must be bf16 [R,H]")
+        if out is None:
+            out = torch.empty((self.T, self.H), dtype=torch.bfloat16, device=self.device)
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.T, self.H), "out must be bf16 [T,H]")
+        if grad_out_probs is not None:
+            self._dev(grad_out_probs, "grad_out_probs")
+            _need(grad_out_probs.dtype == torch.float32 and grad_out_probs.numel() >= self.R,
+                  "grad_out_probs must hold R floats")
+            grad_probs = self._grad_probs_out(grad_probs)
+        else:
+            _need(grad_probs is None, "grad_probs needs grad_out_probs")
+        A.check(A.lib().moe_dispatch_backward(C.byref(self.h), _ptr(grad_out), _ptr(grad_out_probs), _ptr(out),
+                                              _ptr(grad_probs), _stream()), "moe_dispatch_backward")
+        return out, grad_probs
+
+    def combine_backward(self, grad_y: torch.Tensor, expert_out: Optional[torch.Tensor] = None,
+                         apply_probs: bool = True, *, out: Optional[torch.Tensor] = None,
+                         grad_probs: Optional[torch.Tensor] = None, want_probs: bool = True):
+        """Gradients of a combine: (grad_expert_out [R,H] bf16, grad_probs or
+        None).  The probability gradient needs the forward's expert_out."""
+        self._dev(grad_y, "grad_y")
+        _need(grad_y.dtype == torch.bfloat16 and tuple(grad_y.shape) == (self.T, self.H), "grad_y must be bf16 [T,H]")
+        if out is None:
+            out = torch.empty((self.R, self.H), dtype=torch.bfloat16, device=self.device)
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.R, self.H), "out must be bf16 [R,H]")
+        if expert_out is not None:
+            self._dev(expert_out, "expert_out")
+            _need(expert_out.dtype == torch.bfloat16 and tuple(expert_out.shape) == (self.R, self.H),
+                  "expert_out must be bf16 [R,H]")
+        if want_probs or grad_probs is not None:
+            _need(expert_out is not None or not apply_probs, "the probability gradient needs expert_out")
+            grad_probs = self._grad_probs_out(grad_probs)
+        A.check(A.lib().moe_combine_backward(C.byref(self.h), _ptr(grad_y), _ptr(expert_out), 1 if apply_probs else 0,
+                                             _ptr(out), _ptr(grad_probs), _stream()), "moe_combine_backward")
+        return out, grad_probs
+
     def layer(self, x, routing, probs, w1, w2, *, perm=None, scratch=None, expert_out=None, out=None,
               w1_scales=None, w2_scales=None, T_live=None, apply_probs=True):
         """dispatch -> grouped MLP -> combine on the current stream."""

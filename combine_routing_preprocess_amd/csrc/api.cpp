@@ -315,4 +315,35 @@ int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_pro
     return hip_rc(launch_combine(h, d_expert_out, apply_probs ? 1 : 0, d_y, (hipStream_t)stream));
 }
 
+int moe_dispatch_backward(const moe_handle* h, const void* d_grad_out, const float* d_grad_out_probs,
+                          void* d_grad_x, float* d_grad_probs, void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (d.T > 0 && (!d_grad_out || !d_grad_x)) return MOE_EINVAL;
+    if (d_grad_probs && !d_grad_out_probs) return MOE_EINVAL;
+    if ((d_grad_out && !al16(d_grad_out)) || (d_grad_x && !al16(d_grad_x))) return MOE_EALIGN;
+    if ((d_grad_out_probs && !al4(d_grad_out_probs)) || (d_grad_probs && !al4(d_grad_probs))) return MOE_EALIGN;
+    if (d.H % 8) return MOE_ESHAPE;
+    rc = hip_rc(launch_combine(h, d_grad_out, 0, d_grad_x, (hipStream_t)stream));
+    if (rc || !d_grad_probs) return rc;
+    return hip_rc(launch_probs_gather(h, d_grad_out_probs, d_grad_probs, (hipStream_t)stream));
+}
+
+int moe_combine_backward(const moe_handle* h, const void* d_grad_y, const void* d_expert_out,
+                         int32_t apply_probs, void* d_grad_expert_out, float* d_grad_probs, void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (d.T > 0 && (!d_grad_y || !d_grad_expert_out)) return MOE_EINVAL;
+    if (d.T > 0 && d_grad_probs && apply_probs && !d_expert_out) return MOE_EINVAL;
+    if ((d_grad_y && !al16(d_grad_y)) || (d_expert_out && !al16(d_expert_out)) ||
+        (d_grad_expert_out && !al16(d_grad_expert_out)))
+        return MOE_EALIGN;
+    if (d_grad_probs && !al4(d_grad_probs)) return MOE_EALIGN;
+    if (d.H % 8) return MOE_ESHAPE;
+    return hip_rc(launch_combine_backward(h, d_grad_y, d_expert_out, apply_probs ? 1 : 0, d_grad_expert_out,
+                                          d_grad_probs, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,248 @@
+// Backward of dispatch and of combine (token, row and probability gradients).
+//
+// Operation: DeepEP PR #716 "perf: reuse HybridEP routing allgather buffer"
+// (section "Full HybridEP reference validation": hidden-state and probability
+// gradients of the backward-of-dispatch and backward-of-combine) and
+// NeMo-Automodel PR #3931 "perf(moe): sync-free HybridEP dispatch" (section
+// "What does this PR do ?": the combine's backward is a dispatch sized by the
+// same host-known row count, so it needs no host sync either).
+//
+//  * Dispatch backward: a token's gradient is the sum of its kept copies'
+//    row gradients, which is the combine with unit weights (the combine
+//    kernel runs it); the probability gradient of copy (t, j) is its row's
+//    gradient, gathered into the routing's shape.
+//  * Combine backward: one wavefront per token holds the token's gradient
+//    row in registers; for each kept copy it writes w * grad_y to the copy's
+//    row (w = the copy probability, or 1) and, when probabilities were
+//    applied, reduces grad_y . Y[row] in fp32 for the probability gradient
+//    (per lane in column order, then a fixed butterfly across the lanes).
+//  * Probability gradients in a Boolean-map routing live at [t, e]; the
+//    expert of a row is found by binary search of the segment offsets, and
+//    the [T, E] table is cleared by a fill kernel first (no memset node, so
+//    the sequence stays safe to capture in a graph).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// Expert whose segment holds row r: the largest e in [0, E) with
+// seg_off[e] <= r (empty segments share their offset with the next one).
+__device__ __forceinline__ int expert_of(const int64_t* __restrict__ seg_off, int E, int r) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg_off[mid] <= (int64_t)r) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// bf16 of the exact product w * x (one rounding, nearest-even).  The fp32
+// product p is the exact product rounded; the only case where rounding p to
+// bf16 differs from rounding the exact product is p sitting exactly on a bf16
+// midpoint (midpoints are fp32 values) while the exact product is not: the
+// rounding error e = fma(w, x, -p) then says which side the product lies on.
+__device__ __forceinline__ uint32_t bf16_mul_rn(float w, float x) {
+    const float p = w * x;
+    const uint32_t u = __float_as_uint(p);
+    if ((u & 0xffffu) == 0x8000u) {
+        const float e = fmaf(w, x, -p);
+        if (e != 0.f) return (u >> 16) + (((e > 0.f) == (p > 0.f)) ? 1u : 0u);
+    }
+    return f32_to_bf16(p);
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, long long n) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+// Dispatch backward, probabilities: one thread per copy (t, j).
+__global__ __launch_bounds__(256) void k_probs_gather(const int32_t* __restrict__ row_id,
+                                                      const float* __restrict__ grad_row_probs,
+                                                      const int64_t* __restrict__ seg_off, int T, int K, int E,
+                                                      int R, int sparse, float* __restrict__ grad_probs) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)T * K) return;
+    const int r = row_id[i];
+    const bool kept = r >= 0 && r < R;
+    if (!sparse) {
+        grad_probs[i] = kept ? grad_row_probs[r] : 0.f;
+    } else if (kept) {
+        const long long t = i / K;
+        grad_probs[t * E + expert_of(seg_off, E, r)] = grad_row_probs[r];
+    }
+}
+
+// Combine backward: one wavefront per token; NPL = 16-byte chunks per lane
+// held in registers (the row has at most 64 * NPL chunks).
+template <int NPL>
+__global__ __launch_bounds__(256) void k_combine_backward(const u32x4* __restrict__ gy, const u32x4* __restrict__ Y,
+                                                          int T, int K, int E, int nch, int R,
+                                                          const int32_t* __restrict__ row_id,
+                                                          const float* __restrict__ copy_prob, int apply,
+                                                          const int64_t* __restrict__ seg_off, int sparse,
+                                                          u32x4* __restrict__ gY, float* __restrict__ grad_probs) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const bool want_dot = grad_probs != nullptr && apply;
+    u32x4 g[NPL];
+    const u32x4* src = gy + (size_t)t * nch;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int c = lane + 64 * i;
+        g[i] = c < nch ? src[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int j = 0; j < K; ++j) {
+        const int r = row_id[(size_t)t * K + j];
+        const bool kept = r >= 0 && r < R;
+        if (!kept) {
+            if (grad_probs && !sparse && lane == 0) grad_probs[(size_t)t * K + j] = 0.f;
+            continue;
+        }
+        const float w = apply ? copy_prob[(size_t)t * K + j] : 1.f;
+        u32x4* dst = gY + (size_t)r * nch;
+        float dot = 0.f;
+        if (want_dot) {
+            const u32x4* yr = Y + (size_t)r * nch;
+            u32x4 y[NPL];
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+                const int c = lane + 64 * i;
+                y[i] = c < nch ? __builtin_nontemporal_load(yr + c) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < NPL; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    dot = fmaf(bf16_lo(g[i][q]), bf16_lo(y[i][q]), dot);
+                    dot = fmaf(bf16_hi(g[i][q]), bf16_hi(y[i][q]), dot);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nch) {
+                u32x4 o;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    o[q] = bf16_mul_rn(w, bf16_lo(g[i][q])) | (bf16_mul_rn(w, bf16_hi(g[i][q])) << 16);
+                __builtin_nontemporal_store(o, dst + c);
+            }
+        }
+        if (grad_probs) {
+            if (want_dot) {
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+            }
+            if (lane == 0) {
+                const size_t at = sparse ? (size_t)t * E + expert_of(seg_off, E, r) : (size_t)t * K + j;
+                grad_probs[at] = want_dot ? dot : 0.f;
+            }
+        }
+    }
+}
+
+// Same, for rows longer than 64*16 chunks: the gradient row is re-read from
+// cache for every copy instead of being held in registers.
+__global__ __launch_bounds__(256) void k_combine_backward_long(const u32x4* __restrict__ gy,
+                                                               const u32x4* __restrict__ Y, int T, int K, int E,
+                                                               int nch, int R, const int32_t* __restrict__ row_id,
+                                                               const float* __restrict__ copy_prob, int apply,
+                                                               const int64_t* __restrict__ seg_off, int sparse,
+                                                               u32x4* __restrict__ gY, float* __restrict__ grad_probs) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const bool want_dot = grad_probs != nullptr && apply;
+    const u32x4* src = gy + (size_t)t * nch;
+    for (int j = 0; j < K; ++j) {
+        const int r = row_id[(size_t)t * K + j];
+        const bool kept = r >= 0 && r < R;
+        if (!kept) {
+            if (grad_probs && !sparse && lane == 0) grad_probs[(size_t)t * K + j] = 0.f;
+            continue;
+        }
+        const float w = apply ? copy_prob[(size_t)t * K + j] : 1.f;
+        u32x4* dst = gY + (size_t)r * nch;
+        const u32x4* yr = want_dot ? Y + (size_t)r * nch : nullptr;
+        float dot = 0.f;
+        for (int c = lane; c < nch; c += 64) {
+            const u32x4 gv = src[c];
+            if (want_dot) {
+                const u32x4 yv = __builtin_nontemporal_load(yr + c);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    dot = fmaf(bf16_lo(gv[q]), bf16_lo(yv[q]), dot);
+                    dot = fmaf(bf16_hi(gv[q]), bf16_hi(yv[q]), dot);
+                }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = bf16_mul_rn(w, bf16_lo(gv[q])) | (bf16_mul_rn(w, bf16_hi(gv[q])) << 16);
+            __builtin_nontemporal_store(o, dst + c);
+        }
+        if (grad_probs) {
+            if (want_dot) {
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
+            }
+            if (lane == 0) {
+                const size_t at = sparse ? (size_t)t * E + expert_of(seg_off, E, r) : (size_t)t * K + j;
+                grad_probs[at] = want_dot ? dot : 0.f;
+            }
+        }
+    }
+}
+
+constexpr int kNplMax = 16;   // chunks per lane held in registers (rows up to 8192 bf16)
+
+hipError_t fill_zero(float* p, long long n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_probs_gather(const moe_handle* h, const float* grad_row_probs, float* grad_probs,
+                               hipStream_t s) {
+    const moe_desc& d = h->desc;
+    if (d.T == 0) return hipSuccess;
+    const int sparse = d.route_fmt == MOE_ROUTE_SPARSE_BOOL;
+    if (sparse) {
+        hipError_t e = fill_zero(grad_probs, (long long)d.T * d.E, s);
+        if (e != hipSuccess) return e;
+    }
+    const long long n = (long long)d.T * d.K;
+    hipLaunchKernelGGL(k_probs_gather, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h->row_id,
+                       grad_row_probs, h->seg_off, d.T, d.K, d.E, (int)d.out_rows, sparse, grad_probs);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_backward(const moe_handle* h, const void* grad_y, const void* expert_out,
+                                   int apply_probs, void* grad_expert_out, float* grad_probs, hipStream_t s) {
+    const moe_desc& d = h->desc;
+    if (d.T == 0) return hipSuccess;
+    const int sparse = d.route_fmt == MOE_ROUTE_SPARSE_BOOL;
+    if (sparse && grad_probs) {
+        hipError_t e = fill_zero(grad_probs, (long long)d.T * d.E, s);
+        if (e != hipSuccess) return e;
+    }
+    const int nch = d.H * 2 / 16;
+    const dim3 grid((unsigned)((d.T + 3) / 4));
+    if (nch <= 64 * kNplMax) {
+        hipLaunchKernelGGL(k_combine_backward<kNplMax>, grid, dim3(256), 0, s, (const u32x4*)grad_y,
+                           (const u32x4*)expert_out, d.T, d.K, d.E, nch, (int)d.out_rows, h->row_id, h->copy_prob,
+                           apply_probs, h->seg_off, sparse, (u32x4*)grad_expert_out, grad_probs);
+    } else {
+        hipLaunchKernelGGL(k_combine_backward_long, grid, dim3(256), 0, s, (const u32x4*)grad_y,
+                           (const u32x4*)expert_out, d.T, d.K, d.E, nch, (int)d.out_rows, h->row_id, h->copy_prob,
+                           apply_probs, h->seg_off, sparse, (u32x4*)grad_expert_out, grad_probs);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -46,6 +46,12 @@ hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_sca
                           float* out_scales, hipStream_t s);
 hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs, void* y_out,
                           hipStream_t s);
+// backward: probability gradients of a dispatch (row gradients gathered to
+// the routing's shape) and the combine backward (row and probability grads)
+hipError_t launch_probs_gather(const moe_handle* h, const float* grad_row_probs, float* grad_probs,
+                               hipStream_t s);
+hipError_t launch_combine_backward(const moe_handle* h, const void* grad_y, const void* expert_out,
+                                   int apply_probs, void* grad_expert_out, float* grad_probs, hipStream_t s);
 // stage 0: FC1 + SwiGLU (in -> act), stage 1: FC2 (act -> expert_out)
 hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* in, const void* w,
                             void* out, int num_cu, hipStream_t s);

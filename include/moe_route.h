@@ -247,6 +247,43 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
 int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_probs, void* d_y,
                 void* stream);
 
+/* ---- backward (gradients of dispatch and combine) ---------------------------
+ * [P2] "Full HybridEP reference validation" (hidden-state and probability
+ * gradients of the backward-of-dispatch and of the backward-of-combine), [P3]
+ * "What does this PR do ?" (the combine's backward is a dispatch sized by the
+ * same host-known row count: no host sync).  Both reuse the handle of the
+ * forward dispatch; gradients are bf16 rows whatever the forward payload.
+ * Probability gradients have the routing's shape: [T,K] fp32 by slot for
+ * dense routing, [T,E] fp32 by expert for a Boolean map; entries of copies
+ * that were not kept (empty, invalid, duplicate, over capacity, beyond
+ * out_rows) and unrouted entries are 0. */
+
+/* Backward of dispatch.  A token's gradient is the sum, in fp32 and slot
+ * order, of its kept copies' row gradients (one rounding to bf16; 0 if none
+ * was kept), i.e. moe_combine with apply_probs = 0 applied to d_grad_out.
+ *   d_grad_out        [R,H] bf16: gradient of the permuted rows
+ *   d_grad_out_probs  nullable [R] fp32: gradient of the dispatch's per-row
+ *                     probabilities (d_out_probs)
+ *   d_grad_x          [T,H] bf16 out
+ *   d_grad_probs      nullable out (requires d_grad_out_probs): each kept
+ *                     copy's row gradient at its routing position */
+int moe_dispatch_backward(const moe_handle* h, const void* d_grad_out, const float* d_grad_out_probs,
+                          void* d_grad_x, float* d_grad_probs, void* stream);
+
+/* Backward of combine.  With w_tj = the copy probability if apply_probs else
+ * 1, for every kept copy (t, j) at row r = row_id[t,j]:
+ *   d_grad_expert_out[r] = w_tj * d_grad_y[t]   (exact product, one rounding
+ *                          to bf16); rows holding no kept copy are not written
+ *   d_grad_probs at (t, j) = sum over h of d_grad_y[t,h] * d_expert_out[r,h]
+ *                          in fp32 when apply_probs, else 0.
+ *   d_grad_y          [T,H] bf16: gradient of the combine output
+ *   d_expert_out      [R,H] bf16: the forward combine's input; read only for
+ *                     the probability gradient (may be NULL otherwise)
+ *   d_grad_expert_out [R,H] bf16 out
+ *   d_grad_probs      nullable out, the routing's shape */
+int moe_combine_backward(const moe_handle* h, const void* d_grad_y, const void* d_expert_out,
+                         int32_t apply_probs, void* d_grad_expert_out, float* d_grad_probs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,6 +162,27 @@ def test_stale_handle_and_missing_routing_are_rejected_before_launch():
     assert L.moe_route_preprocess(C.byref(h2), C.c_void_p(base + 2), None, None, x, None, x, None) == A.MOE_EALIGN
 
 
+def test_backward_argument_checks_before_launch():
+    L = A.lib()
+    rc, h, base, n, _buf = _host_handle(_desc())
+    assert rc == 0
+    x = C.c_void_p(base)
+    # no routing metadata yet
+    assert L.moe_dispatch_backward(C.byref(h), x, None, x, None, None) == A.MOE_ESTALE
+    assert L.moe_combine_backward(C.byref(h), x, x, 1, x, None, None) == A.MOE_ESTALE
+    h.state = 1   # as if routing had been enqueued; every case below fails its checks first
+    assert L.moe_dispatch_backward(C.byref(h), None, None, x, None, None) == A.MOE_EINVAL
+    assert L.moe_dispatch_backward(C.byref(h), x, None, None, None, None) == A.MOE_EINVAL
+    assert L.moe_dispatch_backward(C.byref(h), x, None, x, x, None) == A.MOE_EINVAL      # grad_probs needs row grads
+    assert L.moe_dispatch_backward(C.byref(h), C.c_void_p(base + 8), None, x, None, None) == A.MOE_EALIGN
+    assert L.moe_dispatch_backward(C.byref(h), x, C.c_void_p(base + 2), x, x, None) == A.MOE_EALIGN
+    assert L.moe_combine_backward(C.byref(h), None, x, 1, x, None, None) == A.MOE_EINVAL
+    assert L.moe_combine_backward(C.byref(h), x, x, 1, None, None, None) == A.MOE_EINVAL
+    assert L.moe_combine_backward(C.byref(h), x, None, 1, x, x, None) == A.MOE_EINVAL    # dot needs expert_out
+    assert L.moe_combine_backward(C.byref(h), x, x, 1, C.c_void_p(base + 4), None, None) == A.MOE_EALIGN
+    assert L.moe_combine_backward(C.byref(h), x, x, 1, x, C.c_void_p(base + 1), None) == A.MOE_EALIGN
+
+
 def test_scratch_sizing():
     d = _desc(T=64, E=4, K=2, pad_multiple=1)
     rc, h, base, n, _buf = _host_handle(d)
