@@ -296,7 +296,22 @@ def _graph_times(step, reps=30):
     return min(t), st.median(t)
 
 
-def _event_times(fn, reps=30, warm=5):
+_FLUSH = []
+
+
+def _flush_caches():
+    """Evict the last-level caches (256 MB memory-side cache, 4 MB L2 per
+    XCD): a 512 MB device copy, enqueued outside any timed region."""
+    import torch
+    if not _FLUSH:
+        _FLUSH.append(torch.empty(2 ** 29, dtype=torch.uint8, device="cuda"))
+        _FLUSH.append(torch.empty(2 ** 29, dtype=torch.uint8, device="cuda"))
+    _FLUSH[1].copy_(_FLUSH[0])
+
+
+def _event_times(fn, reps=30, warm=5, flush=False):
+    """min / median ms of `fn` over `reps` runs; with `flush`, caches are
+    evicted before every run so inputs come from HBM (cold)."""
     import statistics as st
     import torch
     for _ in range(warm):
@@ -304,6 +319,8 @@ def _event_times(fn, reps=30, warm=5):
     torch.cuda.synchronize()
     t = []
     for _ in range(reps):
+        if flush:
+            _flush_caches()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn()
@@ -389,14 +406,48 @@ def run_extra(args):
     y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
     d.preprocess(rt, pt)
     nbytes = (c.T + c.T * c.K) * c.H * 2
-    pm, _ = _event_times(lambda: d.permute(x, out=perm))
-    cm, _ = _event_times(lambda: d.combine(perm, out=y))
+    pm, _ = _event_times(lambda: d.permute(x, out=perm), flush=True)
+    cm, _ = _event_times(lambda: d.combine(perm, out=y), flush=True)
+    pw, _ = _event_times(lambda: d.permute(x, out=perm))
+    cw, _ = _event_times(lambda: d.combine(perm, out=y))
     gm, gmed = _graph_times(lambda: (d.dispatch(x, rt, pt, out=perm), d.combine(perm, out=y)))
     res["cfg2_permute_combine"] = {
-        "capacity": cap, "permute_min_ms": round(pm, 4), "combine_min_ms": round(cm, 4),
+        "capacity": cap, "timing": "cold caches (512 MB copy before each run); warm = repeated runs",
+        "permute_min_ms": round(pm, 4), "combine_min_ms": round(cm, 4),
         "permute_GB_s": round(nbytes / (pm * 1e-3) / 1e9, 1), "combine_GB_s": round(nbytes / (cm * 1e-3) / 1e9, 1),
+        "permute_warm_GB_s": round(nbytes / (pw * 1e-3) / 1e9, 1),
+        "combine_warm_GB_s": round(nbytes / (cw * 1e-3) / 1e9, 1),
         "graph_dispatch_combine_min_ms": round(gm, 4), "graph_median_ms": round(gmed, 4)}
     del d, x, perm, y
+
+    # backward of dispatch and combine at the layer shape (8192 x 7168, 256
+    # experts top-8, padding 128), cold caches
+    c = S.CONFIGS["cfg4_dsv3_layer"]
+    idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
+    d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)
+    d.preprocess(torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(c.seed + 50)
+    G = torch.randn((d.R, c.H), generator=gen, device=dev).to(torch.bfloat16)
+    Yb = torch.randn((d.R, c.H), generator=gen, device=dev).to(torch.bfloat16)
+    gy = torch.randn((c.T, c.H), generator=gen, device=dev).to(torch.bfloat16)
+    gop = torch.randn(d.R, generator=gen, device=dev)
+    gx = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+    gY = torch.empty_like(G)
+    gp = torch.empty((c.T, c.K), dtype=torch.float32, device=dev)
+    gq = torch.empty((c.T, c.K), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    n_copies = int(d.kept.sum().item())
+    db, _ = _event_times(lambda: d.dispatch_backward(G, gop, out=gx, grad_probs=gp), flush=True)
+    cb, _ = _event_times(lambda: d.combine_backward(gy, Yb, True, out=gY, grad_probs=gq), flush=True)
+    db_bytes = n_copies * c.H * 2 + c.T * c.H * 2 + n_copies * 4 + c.T * c.K * 4
+    cb_bytes = c.T * c.H * 2 + 2 * n_copies * c.H * 2 + c.T * c.K * 4
+    res["backward_dsv3_shape"] = {
+        "copies": n_copies, "timing": "cold caches",
+        "dispatch_backward_min_ms": round(db, 4), "dispatch_backward_GB_s": round(db_bytes / (db * 1e-3) / 1e9, 1),
+        "combine_backward_min_ms": round(cb, 4), "combine_backward_GB_s": round(cb_bytes / (cb * 1e-3) / 1e9, 1),
+        "alg_bytes": {"dispatch_backward": db_bytes, "combine_backward": cb_bytes}}
+    del d, G, Yb, gy, gop, gx, gY, gp, gq
 
     # routing stress: 256 experts top-36 Zipf, fp8 payload, dense vs Boolean map
     c = S.CONFIGS["cfg3_route_stress_fp8"]
@@ -410,8 +461,8 @@ def run_extra(args):
         r = torch.from_numpy(routing).to(dev)
         po = torch.empty((d.R, c.H), dtype=torch.uint8, device=dev)
         so = torch.empty((d.R, c.H // 128), dtype=torch.float32, device=dev)
-        km, _ = _event_times(lambda: d.preprocess(r))
-        pmn, _ = _event_times(lambda: d.permute(xq, xs, out=po, out_scales=so))
+        km, _ = _event_times(lambda: d.preprocess(r), flush=True)
+        pmn, _ = _event_times(lambda: d.permute(xq, xs, out=po, out_scales=so), flush=True)
         nb = (c.T + c.T * c.K) * (c.H + 4 * c.H // 128)
         out3[name] = {"preprocess_min_us": round(km * 1e3, 1), "permute_min_ms": round(pmn, 4),
                       "permute_GB_s": round(nb / (pmn * 1e-3) / 1e9, 1)}

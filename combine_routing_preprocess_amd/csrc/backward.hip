@@ -11,11 +11,12 @@
 //    row gradients, which is the combine with unit weights (the combine
 //    kernel runs it); the probability gradient of copy (t, j) is its row's
 //    gradient, gathered into the routing's shape.
-//  * Combine backward: one wavefront per token holds the token's gradient
-//    row in registers; for each kept copy it writes w * grad_y to the copy's
-//    row (w = the copy probability, or 1) and, when probabilities were
-//    applied, reduces grad_y . Y[row] in fp32 for the probability gradient
-//    (per lane in column order, then a fixed butterfly across the lanes).
+//  * Combine backward: the token's gradient row is held in registers by one
+//    to four wavefronts (column slices); for each kept copy they write
+//    w * grad_y to the copy's row (w = the copy probability, or 1) and, when
+//    probabilities were applied, reduce grad_y . Y[row] in fp32 for the
+//    probability gradient (per lane in column order, a fixed butterfly
+//    across the lanes, then the slices in order).
 //  * Probability gradients in a Boolean-map routing live at [t, e]; the
 //    expert of a row is found by binary search of the segment offsets, and
 //    the [T, E] table is cleared by a fill kernel first (no memset node, so
@@ -74,78 +75,102 @@ __global__ __launch_bounds__(256) void k_probs_gather(const int32_t* __restrict_
     }
 }
 
-// Combine backward: one wavefront per token; NPL = 16-byte chunks per lane
-// held in registers (the row has at most 64 * NPL chunks).
+// Combine backward: a token's row is cut into `nsl` column slices of up to
+// 64 * NPL chunks, one wavefront per slice, 4 / nsl tokens per workgroup.
+// Each wavefront holds its slice of grad_y in registers; per copy it issues
+// the expert-output loads, writes the row gradient, then reduces its partial
+// dot product (lane order, then a butterfly) into LDS.  After a workgroup
+// barrier the first wavefront of each token adds the slices' partials in
+// slice order.  Row ids and probabilities are loaded one copy ahead.
 template <int NPL>
 __global__ __launch_bounds__(256) void k_combine_backward(const u32x4* __restrict__ gy, const u32x4* __restrict__ Y,
-                                                          int T, int K, int E, int nch, int R,
+                                                          int T, int K, int E, int nch, int R, int nsl,
                                                           const int32_t* __restrict__ row_id,
                                                           const float* __restrict__ copy_prob, int apply,
                                                           const int64_t* __restrict__ seg_off, int sparse,
                                                           u32x4* __restrict__ gY, float* __restrict__ grad_probs) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    extern __shared__ float part[];   // [4][K] per-wavefront partial dot of each copy
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * (4 / nsl) + wave / nsl;
+    const int sl = wave % nsl;
+    const int cs = sl * 64 * NPL;
+    const bool active = t < T;
     const bool want_dot = grad_probs != nullptr && apply;
-    u32x4 g[NPL];
-    const u32x4* src = gy + (size_t)t * nch;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int c = lane + 64 * i;
-        g[i] = c < nch ? src[c] : u32x4{0u, 0u, 0u, 0u};
-    }
-    for (int j = 0; j < K; ++j) {
-        const int r = row_id[(size_t)t * K + j];
-        const bool kept = r >= 0 && r < R;
-        if (!kept) {
-            if (grad_probs && !sparse && lane == 0) grad_probs[(size_t)t * K + j] = 0.f;
-            continue;
-        }
-        const float w = apply ? copy_prob[(size_t)t * K + j] : 1.f;
-        u32x4* dst = gY + (size_t)r * nch;
-        float dot = 0.f;
-        if (want_dot) {
-            const u32x4* yr = Y + (size_t)r * nch;
-            u32x4 y[NPL];
-#pragma unroll
-            for (int i = 0; i < NPL; ++i) {
-                const int c = lane + 64 * i;
-                y[i] = c < nch ? __builtin_nontemporal_load(yr + c) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int i = 0; i < NPL; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    dot = fmaf(bf16_lo(g[i][q]), bf16_lo(y[i][q]), dot);
-                    dot = fmaf(bf16_hi(g[i][q]), bf16_hi(y[i][q]), dot);
-                }
-        }
+    if (active) {
+        u32x4 g[NPL];
+        const u32x4* src = gy + (size_t)t * nch;
 #pragma unroll
         for (int i = 0; i < NPL; ++i) {
-            const int c = lane + 64 * i;
-            if (c < nch) {
-                u32x4 o;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    o[q] = bf16_mul_rn(w, bf16_lo(g[i][q])) | (bf16_mul_rn(w, bf16_hi(g[i][q])) << 16);
-                __builtin_nontemporal_store(o, dst + c);
-            }
+            const int c = cs + lane + 64 * i;
+            g[i] = c < nch ? src[c] : u32x4{0u, 0u, 0u, 0u};
         }
-        if (grad_probs) {
+        const int32_t* rid = row_id + (size_t)t * K;
+        const float* cp = copy_prob + (size_t)t * K;
+        int r_next = rid[0];
+        float w_next = apply ? cp[0] : 1.f;
+        for (int j = 0; j < K; ++j) {
+            const int r = r_next;
+            const float w = w_next;
+            if (j + 1 < K) {
+                r_next = rid[j + 1];
+                w_next = apply ? cp[j + 1] : 1.f;
+            }
+            if (r < 0 || r >= R) {
+                if (want_dot && lane == 0) part[wave * K + j] = 0.f;
+                continue;
+            }
+            u32x4 y[NPL];
             if (want_dot) {
+                const u32x4* yr = Y + (size_t)r * nch;
+#pragma unroll
+                for (int i = 0; i < NPL; ++i) {
+                    const int c = cs + lane + 64 * i;
+                    y[i] = c < nch ? __builtin_nontemporal_load(yr + c) : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            u32x4* dst = gY + (size_t)r * nch;
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) {
+                const int c = cs + lane + 64 * i;
+                if (c < nch) {
+                    u32x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        o[q] = bf16_mul_rn(w, bf16_lo(g[i][q])) | (bf16_mul_rn(w, bf16_hi(g[i][q])) << 16);
+                    __builtin_nontemporal_store(o, dst + c);
+                }
+            }
+            if (want_dot) {
+                float dot = 0.f;
+#pragma unroll
+                for (int i = 0; i < NPL; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        dot = fmaf(bf16_lo(g[i][q]), bf16_lo(y[i][q]), dot);
+                        dot = fmaf(bf16_hi(g[i][q]), bf16_hi(y[i][q]), dot);
+                    }
 #pragma unroll
                 for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
-            }
-            if (lane == 0) {
-                const size_t at = sparse ? (size_t)t * E + expert_of(seg_off, E, r) : (size_t)t * K + j;
-                grad_probs[at] = want_dot ? dot : 0.f;
+                if (lane == 0) part[wave * K + j] = dot;
             }
         }
+    }
+    if (grad_probs == nullptr) return;   // uniform over the workgroup
+    __syncthreads();
+    if (!active || sl != 0) return;
+    for (int j = lane; j < K; j += 64) {
+        const int r = row_id[(size_t)t * K + j];
+        const bool kept = r >= 0 && r < R;
+        float v = 0.f;
+        if (want_dot && kept)
+            for (int s2 = 0; s2 < nsl; ++s2) v += part[(wave + s2) * K + j];
+        if (!sparse) grad_probs[(size_t)t * K + j] = v;
+        else if (kept) grad_probs[(size_t)t * E + expert_of(seg_off, E, r)] = v;
     }
 }
 
-// Same, for rows longer than 64*16 chunks: the gradient row is re-read from
-// cache for every copy instead of being held in registers.
+// One wavefront per token for rows longer than 4 slices of 64*8 chunks: the
+// gradient row is re-read from cache for every copy.
 __global__ __launch_bounds__(256) void k_combine_backward_long(const u32x4* __restrict__ gy,
                                                                const u32x4* __restrict__ Y, int T, int K, int E,
                                                                int nch, int R, const int32_t* __restrict__ row_id,
@@ -197,7 +222,8 @@ __global__ __launch_bounds__(256) void k_combine_backward_long(const u32x4* __re
     }
 }
 
-constexpr int kNplMax = 16;   // chunks per lane held in registers (rows up to 8192 bf16)
+constexpr int kNpl = 4;       // chunks per lane of a slice held in registers
+constexpr int kMaxSlices = 4; // slices per row (rows up to 4 * 64 * 4 chunks = 8192 bf16)
 
 hipError_t fill_zero(float* p, long long n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
@@ -232,12 +258,16 @@ hipError_t launch_combine_backward(const moe_handle* h, const void* grad_y, cons
         if (e != hipSuccess) return e;
     }
     const int nch = d.H * 2 / 16;
-    const dim3 grid((unsigned)((d.T + 3) / 4));
-    if (nch <= 64 * kNplMax) {
-        hipLaunchKernelGGL(k_combine_backward<kNplMax>, grid, dim3(256), 0, s, (const u32x4*)grad_y,
-                           (const u32x4*)expert_out, d.T, d.K, d.E, nch, (int)d.out_rows, h->row_id, h->copy_prob,
-                           apply_probs, h->seg_off, sparse, (u32x4*)grad_expert_out, grad_probs);
+    const int nsl = nch <= 64 * kNpl ? 1 : nch <= 2 * 64 * kNpl ? 2 : 4;
+    if (nch <= kMaxSlices * 64 * kNpl) {
+        const int tpb = 4 / nsl;
+        const size_t lds = grad_probs ? (size_t)4 * d.K * sizeof(float) : 0;
+        hipLaunchKernelGGL(k_combine_backward<kNpl>, dim3((unsigned)((d.T + tpb - 1) / tpb)), dim3(256), lds, s,
+                           (const u32x4*)grad_y, (const u32x4*)expert_out, d.T, d.K, d.E, nch, (int)d.out_rows, nsl,
+                           h->row_id, h->copy_prob, apply_probs, h->seg_off, sparse, (u32x4*)grad_expert_out,
+                           grad_probs);
     } else {
+        const dim3 grid((unsigned)((d.T + 3) / 4));
         hipLaunchKernelGGL(k_combine_backward_long, grid, dim3(256), 0, s, (const u32x4*)grad_y,
                            (const u32x4*)expert_out, d.T, d.K, d.E, nch, (int)d.out_rows, h->row_id, h->copy_prob,
                            apply_probs, h->seg_off, sparse, (u32x4*)grad_expert_out, grad_probs);
