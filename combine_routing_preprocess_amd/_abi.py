@@ -42,6 +42,7 @@ SIGNATURES = [
     ("moe_handle_init", C.c_int, [C.POINTER(MoeDesc), _P, C.c_size_t, C.POINTER(MoeHandle)]),
     ("moe_route_preprocess", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P, _P, _P, _P]),
     ("moe_permute", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P, _P]),
+    ("moe_permute_quantize", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P]),
     ("moe_dispatch", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     ("moe_mlp_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32, C.c_int32]),
     ("moe_grouped_swiglu_mlp", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P,

@@ -177,6 +177,27 @@ class Dispatcher:
                                     _stream()), "moe_permute")
         return (out, out_scales) if self.payload == A.FP8E4M3_B128 else out
 
+    def permute_quantize(self, x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         out_scales: Optional[torch.Tensor] = None):
+        """Quantise-on-dispatch (handle with fp8 payload): bf16 token rows x
+        [T,H] -> e4m3 codes [R,H] and 1x128 fp32 scales [R,H/128] at every
+        kept copy's row.  Returns (codes, scales)."""
+        _need(self.payload == A.FP8E4M3_B128, "quantise-on-dispatch needs a handle with fp8 payload")
+        self._dev(x, "x")
+        _need(x.dtype == torch.bfloat16 and tuple(x.shape) == (self.T, self.H), "x must be bf16 [T,H]")
+        if out is None:
+            out = torch.empty((self.R, self.H), dtype=torch.uint8, device=self.device)
+        if out_scales is None:
+            out_scales = torch.empty((self.R, self.H // 128), dtype=torch.float32, device=self.device)
+        self._dev(out, "out")
+        self._dev(out_scales, "out_scales")
+        _need(out.dtype in _FP8_DTYPES and tuple(out.shape) == (self.R, self.H), "out must be e4m3 codes [R,H]")
+        _need(out_scales.dtype == torch.float32 and tuple(out_scales.shape) == (self.R, self.H // 128),
+              "out_scales must be float32 [R, H/128]")
+        A.check(A.lib().moe_permute_quantize(C.byref(self.h), _ptr(x), _ptr(out), _ptr(out_scales), _stream()),
+                "moe_permute_quantize")
+        return out, out_scales
+
     def dispatch(self, x: torch.Tensor, routing: torch.Tensor, probs: Optional[torch.Tensor] = None, *,
                  x_scales=None, out=None, out_scales=None, out_probs=None, T_live=None):
         """preprocess + permute.  Returns (permuted, tokens_per_expert, flag,
@@ -201,19 +222,35 @@ class Dispatcher:
         _need(n > 0, "invalid F / wdtype for the MLP scratch")
         return torch.empty(n, dtype=torch.uint8, device=self.device)
 
+    def _check_perm(self, perm, perm_scales):
+        self._dev(perm, "perm")
+        if self.payload == A.FP8E4M3_B128:
+            _need(perm.dtype in _FP8_DTYPES and tuple(perm.shape) == (self.R, self.H),
+                  "perm must be e4m3 codes [R,H] (quantised on dispatch)")
+            _need(perm_scales is not None, "fp8 permuted rows need their scales")
+            self._dev(perm_scales, "perm_scales")
+            _need(perm_scales.dtype == torch.float32 and tuple(perm_scales.shape) == (self.R, self.H // 128),
+                  "perm_scales must be float32 [R, H/128]")
+        else:
+            _need(perm.dtype == torch.bfloat16 and tuple(perm.shape) == (self.R, self.H), "perm must be bf16 [R,H]")
+            _need(perm_scales is None, "bf16 permuted rows take no scales")
+
     def grouped_mlp(self, perm: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, *,
                     w1_scales: Optional[torch.Tensor] = None, w2_scales: Optional[torch.Tensor] = None,
-                    scratch: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+                    scratch: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    perm_scales: Optional[torch.Tensor] = None):
         """Grouped SwiGLU MLP over the permuted rows.  w1 [E,2F,H], w2 [E,H,F]
-        (bf16, or e4m3 codes with 128x128 block scales)."""
+        (bf16, or e4m3 codes with 128x128 block scales).  With a handle of fp8
+        payload, perm is e4m3 codes quantised on dispatch plus perm_scales
+        (fp8 weights only)."""
         fp8w = w1.dtype in _FP8_DTYPES
         wdtype = "fp8" if fp8w else "bf16"
         E, F2, H = w1.shape
         F = F2 // 2
         _need(E == self.E and H == self.H and tuple(w2.shape) == (self.E, self.H, F), "weight shapes")
-        for t, n in ((perm, "perm"), (w1, "w1"), (w2, "w2")):
+        for t, n in ((w1, "w1"), (w2, "w2")):
             self._dev(t, n)
-        _need(perm.dtype == torch.bfloat16 and tuple(perm.shape) == (self.R, self.H), "perm must be bf16 [R,H]")
+        self._check_perm(perm, perm_scales)
         if fp8w:
             _need(w1_scales is not None and w2_scales is not None, "fp8 weights need block scales")
             _need(tuple(w1_scales.shape) == (E, F2 // 128, H // 128) and tuple(w2_scales.shape) == (E, H // 128, F // 128),
@@ -226,17 +263,19 @@ class Dispatcher:
             out = torch.empty((self.R, self.H), dtype=torch.bfloat16, device=self.device)
         self._dev(out, "out")
         _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.R, self.H), "out must be bf16 [R,H]")
-        A.check(A.lib().moe_grouped_swiglu_mlp(C.byref(self.h), F, _DT[wdtype], _ptr(perm), None, _ptr(w1),
+        A.check(A.lib().moe_grouped_swiglu_mlp(C.byref(self.h), F, _DT[wdtype], _ptr(perm), _ptr(perm_scales), _ptr(w1),
                                                _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(scratch),
                                                scratch.numel(), _ptr(out), _stream()), "moe_grouped_swiglu_mlp")
         return out
 
-    def fc1(self, perm: torch.Tensor, w1: torch.Tensor, scratch: torch.Tensor, w1_scales=None) -> None:
+    def fc1(self, perm: torch.Tensor, w1: torch.Tensor, scratch: torch.Tensor, w1_scales=None,
+            perm_scales=None) -> None:
         """FC1 + SwiGLU of every kept row into ``scratch`` (the first half of
         grouped_mlp)."""
         F = w1.shape[1] // 2
         wdtype = "fp8" if w1.dtype in _FP8_DTYPES else "bf16"
-        A.check(A.lib().moe_grouped_fc1_swiglu(C.byref(self.h), F, _DT[wdtype], _ptr(perm), None, _ptr(w1),
+        self._check_perm(perm, perm_scales)
+        A.check(A.lib().moe_grouped_fc1_swiglu(C.byref(self.h), F, _DT[wdtype], _ptr(perm), _ptr(perm_scales), _ptr(w1),
                                                _ptr(w1_scales), _ptr(scratch), scratch.numel(), _stream()),
                 "moe_grouped_fc1_swiglu")
 

@@ -203,6 +203,17 @@ int moe_permute(const moe_handle* h, const void* d_x, const float* d_x_scales, v
     return hip_rc(launch_permute(h, d_x, d_x_scales, d_out, d_out_scales, (hipStream_t)stream));
 }
 
+int moe_permute_quantize(const moe_handle* h, const void* d_x, void* d_out, float* d_out_scales, void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (d.payload != MOE_FP8E4M3_B128) return MOE_EDTYPE;
+    if (d.T > 0 && (!d_x || !d_out || !d_out_scales)) return MOE_EINVAL;
+    if ((d_x && !al16(d_x)) || (d_out && !al16(d_out))) return MOE_EALIGN;
+    if (d_out_scales && !al4(d_out_scales)) return MOE_EALIGN;
+    return hip_rc(launch_permute_quant(h, d_x, d_out, d_out_scales, (hipStream_t)stream));
+}
+
 int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs, const int32_t* d_T_live,
                  const void* d_x, const float* d_x_scales, void* d_out, float* d_out_scales,
                  float* d_out_probs, int32_t* d_tokens_per_expert, int32_t* d_flag, void* stream) {
@@ -240,7 +251,7 @@ int check_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* w, con
     if (rc) return rc;
     const moe_desc& d = h->desc;
     if (F <= 0) return MOE_ESHAPE;
-    if (d.payload != MOE_BF16) return MOE_EDTYPE;
+    if (d.payload != MOE_BF16 && wdtype != MOE_FP8E4M3_B128) return MOE_EDTYPE;
     if (!w || !scratch) return MOE_EINVAL;
     if (!al16(w) || !al16(scratch)) return MOE_EALIGN;
     const size_t need = moe_mlp_scratch_bytes(h, F, wdtype);
@@ -268,11 +279,14 @@ int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const
     int ncu = 0;
     int rc = check_mlp(h, F, wdtype, d_w1, d_w1_scales, d_scratch, scratch_bytes, &ncu);
     if (rc) return rc;
-    if (d_perm_scales) return MOE_EDTYPE;
+    // fp8 permuted rows (quantised on dispatch) carry their scales; bf16 rows none
+    const bool fp8_rows = h->desc.payload == MOE_FP8E4M3_B128;
+    if (fp8_rows != (d_perm_scales != nullptr)) return fp8_rows ? MOE_EINVAL : MOE_EDTYPE;
     if (!d_perm) return MOE_EINVAL;
-    if (!al16(d_perm)) return MOE_EALIGN;
+    if (!al16(d_perm) || (d_perm_scales && !al4(d_perm_scales))) return MOE_EALIGN;
     if (wdtype == MOE_FP8E4M3_B128)
-        return hip_rc(launch_gemm_fp8(h, 0, F, d_perm, d_w1, d_w1_scales, d_scratch, nullptr, (hipStream_t)stream));
+        return hip_rc(launch_gemm_fp8(h, 0, F, d_perm, d_perm_scales, d_w1, d_w1_scales, d_scratch, nullptr,
+                                      (hipStream_t)stream));
     return hip_rc(launch_gemm_bf16(h, 0, F, d_perm, d_w1, d_scratch, ncu, (hipStream_t)stream));
 }
 
@@ -285,7 +299,8 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
     if (!d_expert_out) return MOE_EINVAL;
     if (!al16(d_expert_out)) return MOE_EALIGN;
     if (wdtype == MOE_FP8E4M3_B128)
-        return hip_rc(launch_gemm_fp8(h, 1, F, nullptr, d_w2, d_w2_scales, d_scratch, d_expert_out, (hipStream_t)stream));
+        return hip_rc(launch_gemm_fp8(h, 1, F, nullptr, nullptr, d_w2, d_w2_scales, d_scratch, d_expert_out,
+                                      (hipStream_t)stream));
     return hip_rc(launch_gemm_bf16(h, 1, F, d_scratch, d_w2, d_expert_out, ncu, (hipStream_t)stream));
 }
 

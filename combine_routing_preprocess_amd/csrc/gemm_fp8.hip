@@ -45,10 +45,6 @@ constexpr int kFeat = 64;         // FC1: features per unit (16 per wavefront: g
 constexpr int kFeat2 = 128;       // FC2: output rows per unit (32 per wavefront: two tiles)
 constexpr int kU = 4;             // 128-wide K blocks per load group
 
-__device__ __forceinline__ float e4m3_prep(float v) {   // saturate to the e4m3 range
-    return fminf(fmaxf(v, -448.f), 448.f);
-}
-
 // ---- row quantiser ------------------------------------------------------------
 // Rows r with src_row[r] >= 0 (rows that hold a kept copy): src [R, ncols]
 // (bf16 bit patterns or fp32) -> q [R, ncols] e4m3 codes, qs [R, ncols/128]
@@ -104,16 +100,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(const SRC* __restrict__ src,
             amax = fmaxf(amax, __shfl_xor(amax, 2));
             amax = fmaxf(amax, __shfl_xor(amax, 4));
             amax = fmaxf(amax, __shfl_xor(amax, 8));
-            const float sc = amax > 0.f ? amax / 448.f : 1.f;
+            const float sc = e4m3_scale(amax);
             uint2 out;
-            int p = 0;
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][0] / sc), e4m3_prep(v[it][1] / sc), p, false);
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][2] / sc), e4m3_prep(v[it][3] / sc), p, true);
-            out.x = (uint32_t)p;
-            p = 0;
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][4] / sc), e4m3_prep(v[it][5] / sc), p, false);
-            p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(v[it][6] / sc), e4m3_prep(v[it][7] / sc), p, true);
-            out.y = (uint32_t)p;
+            out.x = e4m3_pack4(v[it][0], v[it][1], v[it][2], v[it][3], sc);
+            out.y = e4m3_pack4(v[it][4], v[it][5], v[it][6], v[it][7], sc);
             *(uint2*)(qr + c) = out;
             if (l16 == 0) qs[(size_t)row * nb + b] = sc;
         }
@@ -269,8 +259,8 @@ size_t fp8_mlp_scratch_bytes(long long R, int H, int F) {
     return up256(r * F * 4) + up256(r * H) + up256(r * (H / 128) * 4) + up256(r * F) + up256(r * (F / 128) * 4);
 }
 
-hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in, const void* w,
-                           const float* ws, void* scratch, void* out, hipStream_t s) {
+hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in, const float* in_scales,
+                           const void* w, const float* ws, void* scratch, void* out, hipStream_t s) {
     const moe_desc& d = h->desc;
     const long long R = d.out_rows;
     if (R == 0) return hipSuccess;
@@ -285,10 +275,17 @@ hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in
         return (unsigned)((R * ngrp + 3) / 4);
     };
     if (stage == 0) {
-        hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(qgrid(d.H)), dim3(256), 0, s, (const uint16_t*)in, d.H, R,
-                           h->src_row, xq, xs);
+        const uint8_t* q = xq;
+        const float* qs = xs;
+        if (in_scales) {   // rows quantised on dispatch
+            q = (const uint8_t*)in;
+            qs = in_scales;
+        } else {
+            hipLaunchKernelGGL(k_quant_rows<uint16_t>, dim3(qgrid(d.H)), dim3(256), 0, s, (const uint16_t*)in, d.H,
+                               R, h->src_row, xq, xs);
+        }
         const int upe = F / kFeat;
-        hipLaunchKernelGGL(k_gemm_fp8<0>, dim3(d.E * upe), dim3(256), 0, s, xq, xs, (const uint8_t*)w, ws, act,
+        hipLaunchKernelGGL(k_gemm_fp8<0>, dim3(d.E * upe), dim3(256), 0, s, q, qs, (const uint8_t*)w, ws, act,
                            h->seg_off, h->kept, R, d.H, 2 * F, F, upe);
     } else {
         hipLaunchKernelGGL(k_quant_rows<float>, dim3(qgrid(F)), dim3(256), 0, s, act, F, R, h->src_row, aq, as);

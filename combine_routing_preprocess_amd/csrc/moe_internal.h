@@ -14,6 +14,7 @@ constexpr int kMaxE = 1024;      // experts supported by the routing kernels
 constexpr int kTileTok = 64;     // tokens per routing tile = one wavefront
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // float -> bf16 bits, round to nearest even (NaN kept quiet).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
@@ -24,6 +25,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---- e4m3 block quantisation (1 x 128 blocks) ------------------------------
+// scale = block amax / 448 (1 for an all-zero block; a correctly rounded fp32
+// division), code = e4m3(v / scale), nearest even, saturating at 448.
+__device__ __forceinline__ float e4m3_prep(float v) {   // saturate to the e4m3 range
+    return fminf(fmaxf(v, -448.f), 448.f);
+}
+__device__ __forceinline__ float e4m3_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
+// Four values -> four e4m3 codes in one 32-bit word (value i in byte i).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float sc) {
+    int p = 0;
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(a / sc), e4m3_prep(b / sc), p, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_prep(c / sc), e4m3_prep(d / sc), p, true);
+    return (uint32_t)p;
+}
 
 // ---- launchers (each returns a hipError_t) --------------------------------
 hipError_t launch_route(const moe_handle* h, const void* routing, const float* probs,
@@ -44,6 +60,8 @@ inline void row_slices(int T, int nch, int* nsplit, int* slice_ch) {
 
 hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_scales, void* out,
                           float* out_scales, hipStream_t s);
+// bf16 token rows -> e4m3 codes + 1x128 scales at every kept copy's row
+hipError_t launch_permute_quant(const moe_handle* h, const void* x, void* out, float* out_scales, hipStream_t s);
 hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs, void* y_out,
                           hipStream_t s);
 // backward: probability gradients of a dispatch (row gradients gathered to
@@ -59,8 +77,10 @@ hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* i
 // (fp32 activations -> bf16 expert output); e4m3 weights with 128x128 scales
 // fp8 path: stage 0 quantises the permuted rows `in` into the scratch and
 // writes fp32 activations there; stage 1 quantises those and writes `out`.
-hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in, const void* w,
-                           const float* ws, void* scratch, void* out, hipStream_t s);
+// With in_scales non-null, stage 0 takes `in` as already quantised rows
+// (e4m3 codes [R,H] with 1x128 scales) and skips the row quantiser.
+hipError_t launch_gemm_fp8(const moe_handle* h, int stage, int F, const void* in, const float* in_scales,
+                           const void* w, const float* ws, void* scratch, void* out, hipStream_t s);
 size_t fp8_mlp_scratch_bytes(long long R, int H, int F);
 
 }  // namespace moe

@@ -186,6 +186,19 @@ int moe_route_preprocess(moe_handle* h, const void* d_routing, const float* d_pr
 int moe_permute(const moe_handle* h, const void* d_x, const float* d_x_scales, void* d_out,
                 float* d_out_scales, void* stream);
 
+/* Quantise-on-dispatch: the permute of bf16 token rows into fp8 rows.  Each
+ * token row is quantised once per 1x128 block (scale = block amax / 448, 1
+ * for an all-zero block; code = e4m3(x / scale), nearest-even, saturating at
+ * 448: the expert MLP's own activation rule) and the codes and scales are
+ * written to every kept copy's row.  [P2] "Full HybridEP reference
+ * validation" (FP8 dispatch), [P1] "Configuration" (FP8 expert GEMMs behind
+ * the dispatch).  Requires desc.payload = MOE_FP8E4M3_B128 (the permuted
+ * rows' format).
+ *   d_x          [T,H] bf16
+ *   d_out        [R,H] e4m3 codes; rows without a copy are not written
+ *   d_out_scales [R,H/128] fp32 */
+int moe_permute_quantize(const moe_handle* h, const void* d_x, void* d_out, float* d_out_scales, void* stream);
+
 /* moe_route_preprocess followed by moe_permute on the same stream. */
 int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs,
                  const int32_t* d_T_live, const void* d_x, const float* d_x_scales, void* d_out,
@@ -205,8 +218,11 @@ size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype);
  * d_expert_out.  [P1] "Summary" and "Configuration" (grouped MLP writing FC2
  * into a caller-provided reusable buffer), [P5] streaming-load commit (FC1
  * weight is the concatenated gate/up matrix).
- *   d_perm        [R,H] bf16 permuted rows (output of moe_permute)
- *   d_perm_scales reserved, must be NULL
+ *   d_perm        [R,H] bf16 permuted rows (output of moe_permute); for a
+ *                 handle with fp8 payload, [R,H] e4m3 codes quantised on
+ *                 dispatch (moe_permute_quantize), fp8 weights only
+ *   d_perm_scales NULL for bf16 rows; [R,H/128] fp32 scales of fp8 rows,
+ *                 which FC1 then consumes without re-quantising
  *   wdtype MOE_BF16: d_w1 [E,2F,H] bf16, d_w2 [E,H,F] bf16, scales NULL;
  *          requires H % 256 == 0 and F % 128 == 0.
  *   wdtype MOE_FP8E4M3_B128: d_w1 [E,2F,H] e4m3, d_w1_scales [E,2F/128,H/128]
