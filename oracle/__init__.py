@@ -69,7 +69,9 @@ def lib():
         L.orc_combine_bf16.restype = None
         L.orc_combine_bf16.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, C.c_int32, P, P]
         L.orc_expert_mlp_bf16.restype = None
-        L.orc_expert_mlp_bf16.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P, P]
+        L.orc_expert_mlp_bf16.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P, P, P]
+        L.orc_combine_fp8.restype = None
+        L.orc_combine_fp8.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, C.c_int32, P, P, P]
         L.orc_quant_rows_e4m3_f32.restype = None
         L.orc_quant_rows_e4m3_f32.argtypes = [C.c_int32, C.c_int32, P, P, P]
         L.orc_expert_mlp_fp8.restype = None
@@ -232,8 +234,11 @@ def combine_backward(grad_y: np.ndarray, Y: np.ndarray, rt: dict, E: int, sparse
     return gY, gp
 
 
-def expert_mlp_bf16(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, return_a: bool = False):
-    """One expert's SwiGLU MLP over rows x [n,H] (bf16 bits); w1 [2F,H], w2 [H,F]."""
+def expert_mlp_bf16(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, return_a: bool = False,
+                    return_y32: bool = False):
+    """One expert's SwiGLU MLP over rows x [n,H] (bf16 bits); w1 [2F,H], w2 [H,F].
+    Returns y (bf16 bits), plus the activations a and/or the FC2 sums rounded
+    to float32 when asked."""
     x = _c(x, np.uint16)
     w1 = _c(w1, np.uint16)
     w2 = _c(w2, np.uint16)
@@ -241,9 +246,25 @@ def expert_mlp_bf16(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, return_a: boo
     F = w1.shape[0] // 2
     y = np.zeros((n, H), np.uint16)
     a = np.zeros((n, F), np.uint16) if return_a else None
+    y32 = np.zeros((n, H), np.float32) if return_y32 else None
     if n:
-        lib().orc_expert_mlp_bf16(n, H, F, _p(x), _p(w1), _p(w2), _p(y), _p(a))
-    return (y, a) if return_a else y
+        lib().orc_expert_mlp_bf16(n, H, F, _p(x), _p(w1), _p(w2), _p(y), _p(a), _p(y32))
+    out = (y,) + ((a,) if return_a else ()) + ((y32,) if return_y32 else ())
+    return out if len(out) > 1 else y
+
+
+def combine_fp8(Yq: np.ndarray, Ys: np.ndarray, row_id: np.ndarray, copy_prob: np.ndarray,
+                apply_probs: bool = True) -> np.ndarray:
+    """Combine from fp8 expert-output rows (e4m3 codes [R,H], scales [R,H/128])."""
+    Yq = _c(Yq, np.uint8)
+    Ys = _c(Ys, np.float32)
+    T, K = row_id.shape
+    H = Yq.shape[1]
+    y = np.zeros((T, H), np.uint16)
+    if T:
+        lib().orc_combine_fp8(T, K, H, _p(_c(row_id, np.int32)), _p(_c(copy_prob, np.float32)),
+                              1 if apply_probs else 0, _p(Yq), _p(Ys), _p(y))
+    return y
 
 
 def quant_rows_e4m3(x: np.ndarray):

@@ -323,6 +323,34 @@ void orc_combine_bf16(int32_t T, int32_t K, int32_t H, const int32_t* row_id,
 }
 
 /* ------------------------------------------------------------------------ */
+/* combine from fp8 expert outputs                                           */
+/* The fp8 combine format: expert-output rows are e4m3 codes with one fp32    */
+/* scale per 128 columns ([P2] "Full HybridEP reference validation": FP8      */
+/* token payloads; [P1] "Configuration": FP8 expert GEMMs).  Each copy's row  */
+/* is dequantised exactly (code value * scale, in double), then combined as   */
+/* in orc_combine_bf16: weighted sum in double, one rounding to bf16.         */
+/* ------------------------------------------------------------------------ */
+void orc_combine_fp8(int32_t T, int32_t K, int32_t H, const int32_t* row_id,
+                     const float* copy_prob, int32_t apply_probs, const uint8_t* Yq,
+                     const float* Ys, uint16_t* y) {
+    const int32_t nb = H / 128;
+#pragma omp parallel for schedule(static)
+    for (int32_t t = 0; t < T; t++) {
+        for (int32_t h = 0; h < H; h++) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < K; j++) {
+                int32_t r = row_id[(int64_t)t * K + j];
+                if (r < 0) continue;
+                double w = apply_probs ? (double)copy_prob[(int64_t)t * K + j] : 1.0;
+                double v = orc_e4m3_to_double(Yq[(int64_t)r * H + h]) * (double)Ys[(int64_t)r * nb + h / 128];
+                acc += w * v;
+            }
+            y[(int64_t)t * H + h] = orc_bf16_from_double(acc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* backward of dispatch                                                      */
 /* [P2] "Full HybridEP reference validation": hidden-state and probability    */
 /* gradients of the backward-of-dispatch communication.  Dispatch copies      */
@@ -410,9 +438,11 @@ void orc_combine_backward(int32_t T, int32_t K, int32_t E, int32_t H, int32_t sp
 /* ------------------------------------------------------------------------ */
 static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* y32 (nullable [n,H]): the FC2 sums rounded once to float, the value an    */
+/* fp8 output format quantises (below, combine in the fp8 format).            */
 void orc_expert_mlp_bf16(int32_t n, int32_t H, int32_t F, const uint16_t* x,
                          const uint16_t* w1, const uint16_t* w2, uint16_t* y,
-                         uint16_t* a_out /* nullable [n,F] */) {
+                         uint16_t* a_out /* nullable [n,F] */, float* y32) {
 #pragma omp parallel
     {
         uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
@@ -437,6 +467,7 @@ void orc_expert_mlp_bf16(int32_t n, int32_t H, int32_t F, const uint16_t* x,
                 for (int32_t i = 0; i < F; i++)
                     acc += orc_bf16_to_double(a[i]) * orc_bf16_to_double(w[i]);
                 y[(int64_t)r * H + o] = orc_bf16_from_double(acc);
+                if (y32) y32[(int64_t)r * H + o] = (float)acc;
             }
         }
         free(a);

@@ -187,3 +187,42 @@ def test_layer_tokens_composes_route_mlp_combine():
     toks = [0, 5, 17, 63]
     part = oracle.layer_tokens(toks, x, rt, lambda e, rows: oracle.expert_mlp_bf16(rows, W1[e], W2[e]))
     assert np.array_equal(part, full[toks])
+
+
+# ---- fp8 combine format -------------------------------------------------------
+def test_expert_mlp_float_output_matches_numpy():
+    """The float32 view of FC2's sums (what an fp8 output format quantises) is
+    the fp64 product of the bf16 activations with W2, rounded once to
+    float32, and rounds to the bf16 output."""
+    n, H, F = 9, 256, 128
+    x = S.bf16_normal((n, H), 71)
+    w1 = S.bf16_normal((2 * F, H), 72, std=0.05)
+    w2 = S.bf16_normal((H, F), 73, std=0.05)
+    y, a, y32 = oracle.expert_mlp_bf16(x, w1, w2, return_a=True, return_y32=True)
+    ref = _f(a) @ _f(w2).T                                  # numpy fp64 from the oracle's own a
+    assert np.all(np.abs(y32.astype(np.float64) - ref) <= 2.0 ** -24 * np.abs(ref) + 1e-30)
+    assert np.mean(_bf16(y32.astype(np.float64)) == y) > 0.999
+
+
+def test_combine_fp8_matches_torch_dequantised_gather():
+    """Dequantise with torch's float8_e4m3fn, weight and sum in fp64 with
+    numpy, round to bf16: the oracle must be that value (nearest rounding)."""
+    r = np.random.default_rng(81)
+    T, K, H, R = 30, 4, 384, 150
+    v = (r.standard_normal((R, H)) * np.exp(r.standard_normal((R, 1)))).astype(np.float32)
+    q, s = oracle.quant_rows_e4m3(v)
+    rid = np.stack([r.choice(R, K, replace=False) for _ in range(T)]).astype(np.int32)
+    rid[r.random((T, K)) < 0.25] = -1
+    cp = r.random((T, K)).astype(np.float32)
+    got = oracle.combine_fp8(q, s, rid, cp)
+    deq = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy() * np.repeat(s, 128, axis=1)
+    w = np.where(rid >= 0, cp.astype(np.float64), 0.0)
+    exact = np.einsum("tk,tkh->th", w, deq[np.maximum(rid, 0)])
+    want = _bf16(exact)
+    ok = (got == want) | (np.abs(_f(got) - exact) <= np.abs(_f(want) - exact))
+    assert ok.all() and np.mean(got == want) > 0.999
+    # without probabilities: the plain sum of the dequantised copies
+    got1 = oracle.combine_fp8(q, s, rid, cp, apply_probs=False)
+    exact1 = np.einsum("tk,tkh->th", (rid >= 0).astype(np.float64), deq[np.maximum(rid, 0)])
+    want1 = _bf16(exact1)
+    assert np.all((got1 == want1) | (np.abs(_f(got1) - exact1) <= np.abs(_f(want1) - exact1)))
