@@ -51,6 +51,9 @@ SIGNATURES = [
                                          C.c_size_t, _P]),
     ("moe_grouped_fc2", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P, _P]),
     ("moe_combine", C.c_int, [C.POINTER(MoeHandle), _P, C.c_int32, _P, _P]),
+    ("moe_grouped_fc2_fp8out", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P,
+                                         _P, _P]),
+    ("moe_combine_fp8", C.c_int, [C.POINTER(MoeHandle), _P, _P, C.c_int32, _P, _P]),
     ("moe_dispatch_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P, _P]),
     ("moe_combine_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, C.c_int32, _P, _P, _P]),
 ]

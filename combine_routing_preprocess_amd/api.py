@@ -288,6 +288,45 @@ class Dispatcher:
                                         scratch.numel(), _ptr(out), _stream()), "moe_grouped_fc2")
         return out
 
+    def fc2_fp8out(self, w2: torch.Tensor, scratch: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   out_scales: Optional[torch.Tensor] = None):
+        """FC2 (bf16 weights) into the fp8 combine format: returns (codes
+        [R,H] uint8, scales [R,H/128] float32)."""
+        self._dev(w2, "w2")
+        _need(w2.dtype == torch.bfloat16 and w2.dim() == 3 and tuple(w2.shape[:2]) == (self.E, self.H),
+              "w2 must be bf16 [E,H,F]")
+        F = w2.shape[2]
+        if out is None:
+            out = torch.empty((self.R, self.H), dtype=torch.uint8, device=self.device)
+        if out_scales is None:
+            out_scales = torch.empty((self.R, self.H // 128), dtype=torch.float32, device=self.device)
+        self._dev(out, "out")
+        self._dev(out_scales, "out_scales")
+        _need(out.dtype in _FP8_DTYPES and tuple(out.shape) == (self.R, self.H), "out must be e4m3 codes [R,H]")
+        _need(out_scales.dtype == torch.float32 and tuple(out_scales.shape) == (self.R, self.H // 128),
+              "out_scales must be float32 [R, H/128]")
+        A.check(A.lib().moe_grouped_fc2_fp8out(C.byref(self.h), F, A.BF16, _ptr(w2), None, _ptr(scratch),
+                                               scratch.numel(), _ptr(out), _ptr(out_scales), _stream()),
+                "moe_grouped_fc2_fp8out")
+        return out, out_scales
+
+    def combine_fp8(self, expert_out_q: torch.Tensor, expert_out_scales: torch.Tensor, apply_probs: bool = True,
+                    out: Optional[torch.Tensor] = None):
+        """Combine from fp8 expert-output rows (codes [R,H], scales [R,H/128])."""
+        self._dev(expert_out_q, "expert_out_q")
+        self._dev(expert_out_scales, "expert_out_scales")
+        _need(expert_out_q.dtype in _FP8_DTYPES and tuple(expert_out_q.shape) == (self.R, self.H),
+              "expert_out_q must be e4m3 codes [R,H]")
+        _need(expert_out_scales.dtype == torch.float32 and tuple(expert_out_scales.shape) == (self.R, self.H // 128),
+              "expert_out_scales must be float32 [R, H/128]")
+        if out is None:
+            out = torch.empty((self.T, self.H), dtype=torch.bfloat16, device=self.device)
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.T, self.H), "out must be bf16 [T,H]")
+        A.check(A.lib().moe_combine_fp8(C.byref(self.h), _ptr(expert_out_q), _ptr(expert_out_scales),
+                                        1 if apply_probs else 0, _ptr(out), _stream()), "moe_combine_fp8")
+        return out
+
     def combine(self, expert_out: torch.Tensor, apply_probs: bool = True, out: Optional[torch.Tensor] = None):
         self._dev(expert_out, "expert_out")
         _need(expert_out.dtype == torch.bfloat16 and tuple(expert_out.shape) == (self.R, self.H),

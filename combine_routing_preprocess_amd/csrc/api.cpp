@@ -287,7 +287,7 @@ int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const
     if (wdtype == MOE_FP8E4M3_B128)
         return hip_rc(launch_gemm_fp8(h, 0, F, d_perm, d_perm_scales, d_w1, d_w1_scales, d_scratch, nullptr,
                                       (hipStream_t)stream));
-    return hip_rc(launch_gemm_bf16(h, 0, F, d_perm, d_w1, d_scratch, ncu, (hipStream_t)stream));
+    return hip_rc(launch_gemm_bf16(h, 0, F, d_perm, d_w1, d_scratch, nullptr, ncu, (hipStream_t)stream));
 }
 
 int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_w2,
@@ -301,7 +301,19 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
     if (wdtype == MOE_FP8E4M3_B128)
         return hip_rc(launch_gemm_fp8(h, 1, F, nullptr, nullptr, d_w2, d_w2_scales, d_scratch, d_expert_out,
                                       (hipStream_t)stream));
-    return hip_rc(launch_gemm_bf16(h, 1, F, d_scratch, d_w2, d_expert_out, ncu, (hipStream_t)stream));
+    return hip_rc(launch_gemm_bf16(h, 1, F, d_scratch, d_w2, d_expert_out, nullptr, ncu, (hipStream_t)stream));
+}
+
+int moe_grouped_fc2_fp8out(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_w2,
+                           const float* d_w2_scales, void* d_scratch, size_t scratch_bytes, void* d_out_q,
+                           float* d_out_scales, void* stream) {
+    int ncu = 0;
+    int rc = check_mlp(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, &ncu);
+    if (rc) return rc;
+    if (wdtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if (!d_out_q || !d_out_scales) return MOE_EINVAL;
+    if (!al16(d_out_q) || !al4(d_out_scales)) return MOE_EALIGN;
+    return hip_rc(launch_gemm_bf16(h, 1, F, d_scratch, d_w2, d_out_q, d_out_scales, ncu, (hipStream_t)stream));
 }
 
 int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
@@ -328,6 +340,19 @@ int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_pro
     if ((d_expert_out && !al16(d_expert_out)) || (d_y && !al16(d_y))) return MOE_EALIGN;
     if (d.H % 8) return MOE_ESHAPE;
     return hip_rc(launch_combine(h, d_expert_out, apply_probs ? 1 : 0, d_y, (hipStream_t)stream));
+}
+
+int moe_combine_fp8(const moe_handle* h, const void* d_expert_out_q, const float* d_expert_out_scales,
+                    int32_t apply_probs, void* d_y, void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (d.H % 128) return MOE_ESHAPE;
+    if (d.T > 0 && (!d_expert_out_q || !d_expert_out_scales || !d_y)) return MOE_EINVAL;
+    if ((d_expert_out_q && !al16(d_expert_out_q)) || (d_y && !al16(d_y))) return MOE_EALIGN;
+    if (d_expert_out_scales && !al4(d_expert_out_scales)) return MOE_EALIGN;
+    return hip_rc(launch_combine_fp8(h, d_expert_out_q, d_expert_out_scales, apply_probs ? 1 : 0, d_y,
+                                     (hipStream_t)stream));
 }
 
 int moe_dispatch_backward(const moe_handle* h, const void* d_grad_out, const float* d_grad_out_probs,

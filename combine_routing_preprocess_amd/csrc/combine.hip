@@ -84,7 +84,101 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ Y, in
     }
 }
 
+// Combine from the fp8 format: expert-output rows are e4m3 codes with one
+// fp32 scale per 128 columns.  Same slicing and copy look-ahead as k_combine;
+// a 16-byte chunk holds 16 codes of one 128-column block, dequantised as
+// code value * scale in fp32 before the probability-weighted fma.
+constexpr int kCombQU = 2;   // 16-byte chunks (16 codes) per lane per pass
+
+__global__ __launch_bounds__(256) void k_combine_fp8(const u32x4* __restrict__ Yq, const float* __restrict__ Ys,
+                                                     int T, int K, int nch, int R, int nsplit, int slice_ch,
+                                                     const int32_t* __restrict__ row_id,
+                                                     const float* __restrict__ copy_prob, int apply,
+                                                     u32x4* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = wv / nsplit;
+    if (t >= T) return;
+    const int cs = (wv - t * nsplit) * slice_ch;
+    const int ce = min(nch, cs + slice_ch);
+    const int nsb = nch / 8;   // scales per row
+    const int32_t* rid = row_id + (size_t)t * K;
+    const float* cp = copy_prob + (size_t)t * K;
+    for (int c0 = cs; c0 < ce; c0 += 64 * kCombQU) {
+        float acc[kCombQU][16];
+#pragma unroll
+        for (int u = 0; u < kCombQU; ++u)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[u][i] = 0.f;
+        for (int j0 = 0; j0 < K; j0 += kCombJ) {
+            u32x4 v[kCombJ][kCombQU];
+            float sc[kCombJ][kCombQU];
+            float pj[kCombJ];
+            bool ok[kCombJ];
+#pragma unroll
+            for (int jj = 0; jj < kCombJ; ++jj) {
+                const int j = j0 + jj;
+                const int r = j < K ? rid[j] : -1;
+                ok[jj] = r >= 0 && r < R;
+                pj[jj] = ok[jj] ? (apply ? cp[j] : 1.f) : 0.f;
+                const size_t rr = (size_t)(ok[jj] ? r : 0);
+#pragma unroll
+                for (int u = 0; u < kCombQU; ++u) {
+                    const int c = c0 + u * 64 + lane;
+                    const bool in = ok[jj] && c < ce;
+                    v[jj][u] = in ? __builtin_nontemporal_load(Yq + rr * nch + c) : u32x4{0u, 0u, 0u, 0u};
+                    sc[jj][u] = in ? Ys[rr * nsb + (c >> 3)] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < kCombJ; ++jj) {
+                if (!ok[jj]) continue;
+#pragma unroll
+                for (int u = 0; u < kCombQU; ++u)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[jj][u][w], false);
+                        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[jj][u][w], true);
+                        const float s_ = sc[jj][u];
+                        acc[u][4 * w + 0] = fmaf(pj[jj], lo[0] * s_, acc[u][4 * w + 0]);
+                        acc[u][4 * w + 1] = fmaf(pj[jj], lo[1] * s_, acc[u][4 * w + 1]);
+                        acc[u][4 * w + 2] = fmaf(pj[jj], hi[0] * s_, acc[u][4 * w + 2]);
+                        acc[u][4 * w + 3] = fmaf(pj[jj], hi[1] * s_, acc[u][4 * w + 3]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCombQU; ++u) {
+            const int c = c0 + u * 64 + lane;
+            if (c < ce) {
+                u32x4 o0, o1;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    o0[w] = f32_to_bf16(acc[u][2 * w]) | (f32_to_bf16(acc[u][2 * w + 1]) << 16);
+                    o1[w] = f32_to_bf16(acc[u][8 + 2 * w]) | (f32_to_bf16(acc[u][8 + 2 * w + 1]) << 16);
+                }
+                y[((size_t)t * nch + c) * 2] = o0;
+                y[((size_t)t * nch + c) * 2 + 1] = o1;
+            }
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_combine_fp8(const moe_handle* h, const void* yq, const float* ys, int apply_probs, void* y_out,
+                              hipStream_t s) {
+    const moe_desc& d = h->desc;
+    if (d.T == 0) return hipSuccess;
+    const int nch = d.H / 16;
+    int nsplit, slice_ch;
+    row_slices(d.T, nch, &nsplit, &slice_ch);
+    const long long waves = (long long)d.T * nsplit;
+    hipLaunchKernelGGL(k_combine_fp8, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, (const u32x4*)yq, ys, d.T,
+                       d.K, nch, (int)d.out_rows, nsplit, slice_ch, h->row_id, h->copy_prob, apply_probs,
+                       (u32x4*)y_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs, void* y_out,
                           hipStream_t s) {

@@ -120,6 +120,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// FC2 output in the fp8 combine format: e4m3 codes [rows, Nout] and one fp32
+// scale per (row, 128 columns); q and s point at the chunk's first row.
+struct QOut {
+    uint8_t* q;
+    float* s;
+};
+
+// Quantise and store one token's 128 output columns held by a lane pair
+// (lanes l and l^32, 64 values each: blocks j = 0..3, 4 groups of 4
+// consecutive columns): block amax over both lanes, scale = amax / 448,
+// nearest-even e4m3 codes.  `cols` is the first of the 128 columns.
+__device__ __forceinline__ void store_q128(const float (&v)[4][16], bool ok, int lane, QOut o, size_t row,
+                                           int Nout, int cols) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(v[j][r]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    if (!ok) return;
+    const float sc = e4m3_scale(amax);
+    uint8_t* qrow = o.q + row * Nout + cols + (lane >> 5) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+            *(uint32_t*)(qrow + j * 32 + g4 * 8) =
+                e4m3_pack4(v[j][g4 * 4], v[j][g4 * 4 + 1], v[j][g4 * 4 + 2], v[j][g4 * 4 + 3], sc);
+    if (lane < 32) o.s[row * (Nout / 128) + cols / 128] = sc;
+}
+
 // One pass: NWB weight blocks (32 rows) per wavefront over the workgroup's
 // 2*NWB weight blocks, NXB token blocks in the chunk, NTB of them (blocks
 // q, q+2, ...) owned by this wavefront.  All threads load; the MFMAs and the
@@ -130,11 +161,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 //   Tokens: DMA instruction b of wavefront w fills LDS chunk slots
 //   256*b + 64*w + lane, i.e. row 32*b + 8*w + lane/8; `xoff`/`xoff_last`
 //   are the per-lane offsets (the last block's rows clamped to the chunk).
-template <int MODE, int NWB, int NXB, int NTB>
+template <int MODE, bool OUTQ, int NWB, int NXB, int NTB>
 __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, const int (&wrow)[2 * NWB],
                                      gchar* xbase, uint32_t voff, uint32_t xoff, uint32_t xoff_last, int pitch,
                                      int nk, int lane, int wave, int p, int q, int mv, uint16_t* obase, int Nout,
-                                     int ocol0) {
+                                     int ocol0, QOut qo) {
     constexpr int NWL = 2 * NWB;   // weight loads per thread per stage (one per block of 32 rows)
     // LDS write slot of this thread's chunk within a block (same for every block)
     const int tid = threadIdx.x;
@@ -259,7 +290,17 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
     // 8*(r/4) + 4*(lane/32) + r%4 of each weight block
     auto store_block = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        if constexpr (i < NTB) {
+        if constexpr (i < NTB && OUTQ) {
+            static_assert(MODE == 1 && NWB == 4, "fp8 output: FC2, 128 columns per wavefront");
+            __builtin_amdgcn_sched_barrier(0);
+            const int tok = (q + 2 * i) * 32 + (lane & 31);
+            float v[4][16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[j][r] = acc_read(acc[j][i][r]);
+            store_q128(v, tok < mv, lane, qo, (size_t)tok, Nout, ocol0);
+        } else if constexpr (i < NTB) {
             __builtin_amdgcn_sched_barrier(0);
             const int tok = (q + 2 * i) * 32 + (lane & 31);
             if (tok < mv) {
@@ -307,9 +348,10 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
 // Weight-row offsets of the pass over features/columns [f0, f0 + 32*2*NWB/(MODE==0 ? 2 : 1))
 // and token-row offsets of the chunk, then the pass itself for this
 // wavefront's token-block count.
-template <int MODE, int NWB, int NXB>
+template <int MODE, bool OUTQ, int NWB, int NXB>
 __device__ __forceinline__ void run_pass(u32x4* wlds, u32x4* xlds, const char* We, const char* Xc, int Kdim,
-                                         int Nout, int f0, int mv, uint16_t* ochunk, int lane, int p, int q) {
+                                         int Nout, int f0, int mv, uint16_t* ochunk, QOut qo, int lane, int p,
+                                         int q) {
     const int tid = threadIdx.x;
     const int r8 = tid >> 3, c8 = (tid & 7) * 16;   // row within a 32-row block, byte offset of the chunk
     // first weight row of each 32-row block of the pass (blocks never straddle
@@ -338,13 +380,13 @@ __device__ __forceinline__ void run_pass(u32x4* wlds, u32x4* xlds, const char* W
     const int nk = Kdim / BK;
     const int ocol0 = MODE == 0 ? f0 + p * 16 * NWB : f0 + p * 32 * NWB;
     if (q == 0)
-        pass<MODE, NWB, NXB, (NXB + 1) / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff, xoff_last,
-                                            pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p, q, mv, ochunk,
-                                            Nout, ocol0);
+        pass<MODE, OUTQ, NWB, NXB, (NXB + 1) / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff,
+                                                  xoff_last, pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p,
+                                                  q, mv, ochunk, Nout, ocol0, qo);
     else
-        pass<MODE, NWB, NXB, NXB / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff, xoff_last,
-                                      pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p, q, mv, ochunk, Nout,
-                                      ocol0);
+        pass<MODE, OUTQ, NWB, NXB, NXB / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff,
+                                            xoff_last, pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p, q,
+                                            mv, ochunk, Nout, ocol0, qo);
 }
 
 // ---- 128-row passes (segments of 257..320 rows) ------------------------------
@@ -497,9 +539,9 @@ __device__ __forceinline__ void mainloop(u32x4* xring, u32x4* wring, const uint1
 // One 128-row pass of unit rows: weights from We (expert base), features
 // (FC1) / columns (FC2) starting at n0, over a chunk of me_c rows starting at
 // token row X (segment row m0 = 0 of the chunk), output rows Out.
-template <int MODE>
+template <int MODE, bool OUTQ>
 __device__ __forceinline__ void half_pass(u32x4* xring, u32x4* wring, const uint16_t* X, const uint16_t* Wb,
-                                          uint16_t* Out, long long seg, int me, int Kdim, int Nout, int n0,
+                                          uint16_t* Out, QOut qo, long long seg, int me, int Kdim, int Nout, int n0,
                                           int wave, int lane) {
     // weight DMA q of wavefront w fills slots (q*4+w)*64.. of a stage:
         // rows 8*(q*4+w)..+7, each lane the logical chunk of its slot
@@ -551,6 +593,16 @@ __device__ __forceinline__ void half_pass(u32x4* xring, u32x4* wring, const uint
             for (int i = 0; i < TBW; ++i) {
                 __builtin_amdgcn_sched_barrier(0);
                 const int tok = (wave + 4 * i) * 32 + (lane & 31);
+                if constexpr (OUTQ) {
+                    if (i >= ntb) continue;          // wave-uniform
+                    float v[4][16];
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) v[nb][r] = acc_read(acc[nb][i][r]);
+                    store_q128(v, tok < mv, lane, qo, (size_t)(seg + m0 + tok), Nout, n0);
+                    continue;
+                }
                 if (i >= ntb || tok >= mv) continue;
                 uint16_t* orow = Out + (size_t)(seg + m0 + tok) * Nout + n0;
                 if (MODE == 0) {
@@ -584,11 +636,13 @@ __device__ __forceinline__ void half_pass(u32x4* xring, u32x4* wring, const uint
         }
 }
 
-template <int MODE>  // 0: FC1 + SwiGLU (out = act [R,F]); 1: FC2 (out = expert_out [R,H])
+// MODE 0: FC1 + SwiGLU (out = act [R,F]); 1: FC2 (out = expert_out [R,H]);
+// OUTQ (FC2 only): the output goes to Oq / Os in the fp8 combine format.
+template <int MODE, bool OUTQ>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_bf16(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Out,
-    const int64_t* __restrict__ seg_off, const int32_t* __restrict__ kept, int E, long long R, int Kdim,
-    int Wrows, int Nout, int n_units) {
+    uint8_t* __restrict__ Oq, float* __restrict__ Os, const int64_t* __restrict__ seg_off,
+    const int32_t* __restrict__ kept, int E, long long R, int Kdim, int Wrows, int Nout, int n_units) {
     __shared__ u32x4 wlds[2 * W_SLOT];
     __shared__ u32x4 xlds[2 * X_SLOT];
     __shared__ int s_list[kMaxE];      // active experts of this XCD, ascending
@@ -638,11 +692,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         for (int m0 = 0; m0 < me; ) {
             const int left = me - m0;
             const char* Xc = (const char*)(X + (size_t)(seg + m0) * Kdim);
-            uint16_t* oc = Out + (size_t)(seg + m0) * Nout;
+            uint16_t* oc = OUTQ ? nullptr : Out + (size_t)(seg + m0) * Nout;
+            const QOut qc = {OUTQ ? Oq + (size_t)(seg + m0) * Nout : nullptr,
+                             OUTQ ? Os + (size_t)(seg + m0) * (Nout / 128) : nullptr};
             if (left <= XROWS_A) {
                 const int mv = left, nblk = (mv + 31) / 32;
                 switch (nblk) {
-#define MOE_A(NB) case NB: run_pass<MODE, 4, NB>(wlds, xlds, We, Xc, Kdim, Nout, u0, mv, oc, lane, p, q); break;
+#define MOE_A(NB) case NB: run_pass<MODE, OUTQ, 4, NB>(wlds, xlds, We, Xc, Kdim, Nout, u0, mv, oc, qc, lane, p, q); break;
                     MOE_A(1) MOE_A(2) MOE_A(3) MOE_A(4) MOE_A(5) MOE_A(6) MOE_A(7) default: MOE_A(8)
 #undef MOE_A
                 }
@@ -651,9 +707,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 // 257..320 rows: two 128-row passes with the token chunk in L2
                 const int mv = min(left, XROWS_B);
                 const uint16_t* Wb = W + (size_t)e * Wrows * Kdim;
+                const QOut qall = {Oq, Os};
                 for (int h = 0; h < 2; ++h)
-                    half_pass<MODE>(xlds, wlds, X, Wb, Out, seg + m0, mv, Kdim, Nout,
-                                    u0 + h * (MODE == 0 ? 64 : 128), wave, lane);
+                    half_pass<MODE, OUTQ>(xlds, wlds, X, Wb, Out, qall, seg + m0, mv, Kdim, Nout,
+                                          u0 + h * (MODE == 0 ? 64 : 128), wave, lane);
                 m0 += mv;
             }
         }
@@ -663,18 +720,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* in, const void* w,
-                            void* out, int num_cu, hipStream_t s) {
+                            void* out, float* out_scales, int num_cu, hipStream_t s) {
     const moe_desc& d = h->desc;
     const long long R = d.out_rows;
     if (R == 0) return hipSuccess;
     int grid = num_cu - num_cu % kNxcd;
     if (grid < kNxcd) grid = num_cu;
     if (stage == 0) {
-        hipLaunchKernelGGL(k_gemm_bf16<0>, dim3(grid), dim3(256), 0, s, (const uint16_t*)in, (const uint16_t*)w,
-                           (uint16_t*)out, h->seg_off, h->kept, d.E, R, d.H, 2 * F, F, F / 128);
-    } else {
-        hipLaunchKernelGGL(k_gemm_bf16<1>, dim3(grid), dim3(256), 0, s, (const uint16_t*)in, (const uint16_t*)w,
-                           (uint16_t*)out, h->seg_off, h->kept, d.E, R, F, d.H, d.H, d.H / 256);
+        hipLaunchKernelGGL((k_gemm_bf16<0, false>), dim3(grid), dim3(256), 0, s, (const uint16_t*)in,
+                           (const uint16_t*)w, (uint16_t*)out, nullptr, nullptr, h->seg_off, h->kept, d.E, R, d.H,
+                           2 * F, F, F / 128);
+    } else if (!out_scales) {
+        hipLaunchKernelGGL((k_gemm_bf16<1, false>), dim3(grid), dim3(256), 0, s, (const uint16_t*)in,
+                           (const uint16_t*)w, (uint16_t*)out, nullptr, nullptr, h->seg_off, h->kept, d.E, R, F, d.H,
+                           d.H, d.H / 256);
+    } else {   // FC2 into the fp8 combine format: out = e4m3 codes [R,H], out_scales [R,H/128]
+        hipLaunchKernelGGL((k_gemm_bf16<1, true>), dim3(grid), dim3(256), 0, s, (const uint16_t*)in,
+                           (const uint16_t*)w, nullptr, (uint8_t*)out, out_scales, h->seg_off, h->kept, d.E, R, F,
+                           d.H, d.H, d.H / 256);
     }
     return hipGetLastError();
 }

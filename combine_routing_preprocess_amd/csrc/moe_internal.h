@@ -64,15 +64,19 @@ hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_sca
 hipError_t launch_permute_quant(const moe_handle* h, const void* x, void* out, float* out_scales, hipStream_t s);
 hipError_t launch_combine(const moe_handle* h, const void* y_in, int apply_probs, void* y_out,
                           hipStream_t s);
+// combine from fp8 expert-output rows (e4m3 codes [R,H] + 1x128 scales)
+hipError_t launch_combine_fp8(const moe_handle* h, const void* yq, const float* ys, int apply_probs, void* y_out,
+                              hipStream_t s);
 // backward: probability gradients of a dispatch (row gradients gathered to
 // the routing's shape) and the combine backward (row and probability grads)
 hipError_t launch_probs_gather(const moe_handle* h, const float* grad_row_probs, float* grad_probs,
                                hipStream_t s);
 hipError_t launch_combine_backward(const moe_handle* h, const void* grad_y, const void* expert_out,
                                    int apply_probs, void* grad_expert_out, float* grad_probs, hipStream_t s);
-// stage 0: FC1 + SwiGLU (in -> act), stage 1: FC2 (act -> expert_out)
+// stage 0: FC1 + SwiGLU (in -> act), stage 1: FC2 (act -> expert_out); with
+// out_scales non-null, FC2 writes e4m3 codes to `out` and 1x128 scales
 hipError_t launch_gemm_bf16(const moe_handle* h, int stage, int F, const void* in, const void* w,
-                            void* out, int num_cu, hipStream_t s);
+                            void* out, float* out_scales, int num_cu, hipStream_t s);
 // stage 0: FC1 + SwiGLU (bf16 rows -> fp32 activations), stage 1: FC2
 // (fp32 activations -> bf16 expert output); e4m3 weights with 128x128 scales
 // fp8 path: stage 0 quantises the permuted rows `in` into the scratch and

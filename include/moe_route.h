@@ -253,6 +253,19 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
                     const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
                     void* d_expert_out, void* stream);
 
+/* FC2 into the fp8 combine format: as moe_grouped_fc2 (bf16 weights), but each
+ * kept row's fp32 output is quantised per 1x128 block (scale = block amax /
+ * 448, 1 for an all-zero block; code = e4m3(y / scale), nearest-even,
+ * saturating) instead of being rounded to bf16, halving the expert-output
+ * bytes that FC2 writes and the combine reads.  [P2] "Full HybridEP reference
+ * validation" (FP8 token payloads), [P1] "Configuration" (FP8 expert GEMMs).
+ *   wdtype        MOE_BF16 only (else MOE_EUNSUPPORTED)
+ *   d_out_q       [R,H] e4m3 codes out; rows without a kept copy not written
+ *   d_out_scales  [R,H/128] fp32 out */
+int moe_grouped_fc2_fp8out(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_w2,
+                           const float* d_w2_scales, void* d_scratch, size_t scratch_bytes, void* d_out_q,
+                           float* d_out_scales, void* stream);
+
 /* Combine-unpermute: y[t] = bf16( sum over the token's surviving copies j, in
  * slot order, of p_tj * expert_out[row_id[t,j]] ) accumulated in fp32;
  * p_tj = copy probability if apply_probs else 1; a token with no surviving
@@ -262,6 +275,15 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
  *   d_y           [T,H] bf16 out */
 int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_probs, void* d_y,
                 void* stream);
+
+/* Combine from the fp8 format: as moe_combine, with each copy's row
+ * dequantised (code value * its block's scale, in fp32) before the weighted
+ * sum.  Requires H % 128 == 0.
+ *   d_expert_out_q       [R,H] e4m3 codes (moe_grouped_fc2_fp8out)
+ *   d_expert_out_scales  [R,H/128] fp32
+ *   d_y                  [T,H] bf16 out */
+int moe_combine_fp8(const moe_handle* h, const void* d_expert_out_q, const float* d_expert_out_scales,
+                    int32_t apply_probs, void* d_y, void* stream);
 
 /* ---- backward (gradients of dispatch and combine) ---------------------------
  * [P2] "Full HybridEP reference validation" (hidden-state and probability
