@@ -449,6 +449,62 @@ def run_extra(args):
         "alg_bytes": {"dispatch_backward": db_bytes, "combine_backward": cb_bytes}}
     del d, G, Yb, gy, gop, gx, gY, gp, gq
 
+    # fp8 formats at the layer shape: quantise-on-dispatch, FC2 into the fp8
+    # combine format and the fp8 combine, against their bf16 counterparts
+    c = S.CONFIGS["cfg4_dsv3_layer"]
+    idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
+    rt, pt = torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev)
+    x = torch.from_numpy(S.bf16_normal((c.T, c.H), c.seed).view(np.int16)).to(dev).view(torch.bfloat16)
+    w1 = S.weights_bf16(c.E, 2 * c.F, c.H, c.seed + 1, device=dev)
+    w2 = S.weights_bf16(c.E, c.H, c.F, c.seed + 2, device=dev)
+    dq = Dispatcher(c.T, c.H, c.E, c.K, payload="fp8", pad_multiple=c.pad)
+    dq.preprocess(rt, pt)
+    pq = torch.empty((dq.R, c.H), dtype=torch.uint8, device=dev)
+    ps = torch.empty((dq.R, c.H // 128), dtype=torch.float32, device=dev)
+    d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)
+    perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+    d.dispatch(x, rt, pt, out=perm)
+    scr = d.alloc_mlp_scratch(c.F)
+    eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+    eq = torch.empty((d.R, c.H), dtype=torch.uint8, device=dev)
+    es = torch.empty((d.R, c.H // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+    d.fc1(perm, w1, scr)
+    torch.cuda.synchronize()
+    n_copies = int(d.kept.sum().item())
+    row8 = c.H + 4 * c.H // 128
+    pqm, _ = _event_times(lambda: dq.permute_quantize(x, out=pq, out_scales=ps), flush=True)
+    f2b, _ = _event_times(lambda: d.fc2(w2, scr, eo), reps=10, warm=2)
+    f2q, _ = _event_times(lambda: d.fc2_fp8out(w2, scr, out=eq, out_scales=es), reps=10, warm=2)
+    cbm, _ = _event_times(lambda: d.combine(eo, out=y), flush=True)
+    cqm, _ = _event_times(lambda: d.combine_fp8(eq, es, out=y), flush=True)
+
+    def layer_q():
+        d.dispatch(x, rt, pt, out=perm)
+        d.fc1(perm, w1, scr)
+        d.fc2_fp8out(w2, scr, out=eq, out_scales=es)
+        d.combine_fp8(eq, es, out=y)
+
+    def layer_b():
+        d.dispatch(x, rt, pt, out=perm)
+        d.fc1(perm, w1, scr)
+        d.fc2(w2, scr, eo)
+        d.combine(eo, out=y)
+
+    lq, _ = _event_times(layer_q, reps=8, warm=2)
+    lb, _ = _event_times(layer_b, reps=8, warm=2)
+    qb = c.T * c.H * 2 + n_copies * row8
+    cb8 = n_copies * row8 + c.T * c.H * 2
+    res["fp8_formats_dsv3_shape"] = {
+        "timing": "row copies with cold caches; GEMMs and layers warm (25 GB of weights stream anyway)",
+        "permute_quantize_min_ms": round(pqm, 4), "permute_quantize_GB_s": round(qb / (pqm * 1e-3) / 1e9, 1),
+        "fc2_bf16_out_min_ms": round(f2b, 4), "fc2_fp8_out_min_ms": round(f2q, 4),
+        "combine_bf16_min_ms": round(cbm, 4), "combine_fp8_min_ms": round(cqm, 4),
+        "combine_fp8_GB_s": round(cb8 / (cqm * 1e-3) / 1e9, 1),
+        "layer_bf16_combine_min_ms": round(lb, 4), "layer_fp8_combine_min_ms": round(lq, 4),
+        "alg_bytes": {"permute_quantize": qb, "combine_fp8": cb8}}
+    del dq, pq, ps, d, perm, scr, eo, eq, es, y, w1, w2, x
+
     # routing stress: 256 experts top-36 Zipf, fp8 payload, dense vs Boolean map
     c = S.CONFIGS["cfg3_route_stress_fp8"]
     idx, _ = S.route_zipf_gumbel(c.T, c.E, c.K, c.seed)
