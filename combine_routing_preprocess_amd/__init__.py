@@ -7,8 +7,8 @@ Every step runs in the hand-written HIP kernels of ``libmoe_route.so``
 """
 from ._abi import (BF16, FP8E4M3_B128, FLAG_BAD_EXPERT, FLAG_CAPACITY, FLAG_DUPLICATE, FLAG_OUT_ROWS,
                    ROUTE_DENSE_I16, ROUTE_DENSE_I32, ROUTE_SPARSE_BOOL, MoeError, lib)
-from .api import (Dispatcher, assert_no_overflow, capacity_from_rows, out_rows_bound, routing_bytes)
+from .api import (BufferRing, Dispatcher, assert_no_overflow, capacity_from_rows, out_rows_bound, routing_bytes)
 
-__all__ = ["Dispatcher", "assert_no_overflow", "capacity_from_rows", "out_rows_bound", "routing_bytes",
+__all__ = ["BufferRing", "Dispatcher", "assert_no_overflow", "capacity_from_rows", "out_rows_bound", "routing_bytes",
            "MoeError", "lib", "BF16", "FP8E4M3_B128", "ROUTE_DENSE_I16", "ROUTE_DENSE_I32",
            "ROUTE_SPARSE_BOOL", "FLAG_CAPACITY", "FLAG_OUT_ROWS", "FLAG_BAD_EXPERT", "FLAG_DUPLICATE"]

@@ -10,6 +10,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_route.so")
 
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EALIGN = 0, -1, -2, -3, -4
 MOE_ESTALE, MOE_EHIP, MOE_EUNSUPPORTED, MOE_ENOSPC = -5, -6, -7, -8
+MOE_EBUSY, MOE_ESTATE = -9, -10
+RING_MAX_SLOTS = 32
 
 ROUTE_DENSE_I16, ROUTE_DENSE_I32, ROUTE_SPARSE_BOOL = 0, 1, 2
 BF16, FP8E4M3_B128 = 0, 1
@@ -29,6 +31,13 @@ class MoeHandle(C.Structure):
                 ("tile_mask", C.c_void_p), ("tile_base", C.c_void_p), ("tile_err", C.c_void_p),
                 ("seg_off", C.c_void_p), ("kept", C.c_void_p), ("rows_needed", C.c_void_p),
                 ("row_id", C.c_void_p), ("copy_prob", C.c_void_p), ("src_row", C.c_void_p)]
+
+
+class MoeRing(C.Structure):
+    _fields_ = [("base", C.c_void_p), ("slot_bytes", C.c_size_t), ("n_slots", C.c_int32), ("next", C.c_int32),
+                ("acquisitions", C.c_uint64), ("state", C.c_int32 * RING_MAX_SLOTS),
+                ("event_kind", C.c_int32 * RING_MAX_SLOTS), ("event_capture", C.c_ulonglong * RING_MAX_SLOTS),
+                ("event", C.c_void_p * RING_MAX_SLOTS)]
 
 
 # (name, restype, argtypes) for every function the header declares
@@ -54,6 +63,10 @@ SIGNATURES = [
     ("moe_grouped_fc2_fp8out", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P,
                                          _P, _P]),
     ("moe_combine_fp8", C.c_int, [C.POINTER(MoeHandle), _P, _P, C.c_int32, _P, _P]),
+    ("moe_ring_init", C.c_int, [C.POINTER(MoeRing), _P, C.c_size_t, C.c_int32]),
+    ("moe_ring_acquire", C.c_int, [C.POINTER(MoeRing), _P, C.POINTER(C.c_void_p), C.POINTER(C.c_int32)]),
+    ("moe_ring_release", C.c_int, [C.POINTER(MoeRing), C.c_int32, _P]),
+    ("moe_ring_destroy", C.c_int, [C.POINTER(MoeRing)]),
     ("moe_dispatch_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P, _P]),
     ("moe_combine_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, C.c_int32, _P, _P, _P]),
 ]

@@ -403,3 +403,45 @@ class Dispatcher:
         y = self.grouped_mlp(perm, w1, w2, w1_scales=w1_scales, w2_scales=w2_scales, scratch=scratch,
                              out=expert_out)
         return self.combine(y, apply_probs=apply_probs, out=out)
+
+
+class BufferRing:
+    """Caller-owned ring of persistent device slots (dispatch outputs, FC2
+    outputs): ``acquire`` hands the next slot to a producer on the current
+    stream, which first waits on the device for the slot's last release;
+    ``release`` marks the final consumer's use on its stream.  Reuse before
+    release raises (MOE_EBUSY), as does a second release (MOE_ESTATE).  The
+    storage is one torch allocation made here; the library only carves it."""
+
+    def __init__(self, n_slots: int, shape, dtype: torch.dtype, device=None):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        n = 1
+        for v in self.shape:
+            n *= int(v)
+        self.nbytes = n * torch.empty(0, dtype=dtype).element_size()
+        self.slot_bytes = (self.nbytes + 255) // 256 * 256
+        self.storage = torch.empty(n_slots * self.slot_bytes, dtype=torch.uint8, device=self.device)
+        self.r = A.MoeRing()
+        A.check(A.lib().moe_ring_init(C.byref(self.r), _ptr(self.storage), self.slot_bytes, int(n_slots)),
+                "moe_ring_init")
+        self.n_slots = n_slots
+
+    def acquire(self, stream=None):
+        """(slot index, tensor view of the slot) for a producer on ``stream``
+        (default: the current stream)."""
+        st = C.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
+        ptr = C.c_void_p()
+        idx = C.c_int32()
+        A.check(A.lib().moe_ring_acquire(C.byref(self.r), st, C.byref(ptr), C.byref(idx)), "moe_ring_acquire")
+        off = int(idx.value) * self.slot_bytes
+        view = self.storage[off:off + self.nbytes].view(self.dtype).view(self.shape)
+        return int(idx.value), view
+
+    def release(self, slot: int, stream=None):
+        st = C.c_void_p((stream or torch.cuda.current_stream()).cuda_stream)
+        A.check(A.lib().moe_ring_release(C.byref(self.r), int(slot), st), "moe_ring_release")
+
+    def close(self):
+        A.check(A.lib().moe_ring_destroy(C.byref(self.r)), "moe_ring_destroy")

@@ -113,6 +113,8 @@ const char* moe_status_string(int status) {
         case MOE_EHIP: return "HIP runtime error";
         case MOE_EUNSUPPORTED: return "not supported";
         case MOE_ENOSPC: return "workspace or scratch too small";
+        case MOE_EBUSY: return "ring slot still in use (reused before its release)";
+        case MOE_ESTATE: return "ring slot not acquired (double release)";
         default: return "unknown status";
     }
 }

@@ -52,7 +52,9 @@ enum moe_status {
                             /* handle has no routing metadata yet             */
     MOE_EHIP = -6,          /* a HIP runtime call failed                       */
     MOE_EUNSUPPORTED = -7,  /* legal but not implemented                       */
-    MOE_ENOSPC = -8         /* workspace or scratch smaller than required      */
+    MOE_ENOSPC = -8,        /* workspace or scratch smaller than required      */
+    MOE_EBUSY = -9,         /* ring slot still in use (reuse before release)   */
+    MOE_ESTATE = -10        /* ring slot released twice / never acquired       */
 };
 
 /* ---- routing formats ([P2] "Memory impact", "Implementation") -------------
@@ -321,6 +323,53 @@ int moe_dispatch_backward(const moe_handle* h, const void* d_grad_out, const flo
  *   d_grad_probs      nullable out, the routing's shape */
 int moe_combine_backward(const moe_handle* h, const void* d_grad_y, const void* d_expert_out,
                          int32_t apply_probs, void* d_grad_expert_out, float* d_grad_probs, void* stream);
+
+/* ---- caller-owned buffer ring ------------------------------------------------
+ * [P1] "Summary", "Motivation", "Known limitations": dispatch outputs and FC2
+ * outputs live in a fixed ring of persistent slots owned by the application;
+ * the final consumer of a slot releases it by recording an event on its own
+ * stream, and the next producer of that slot waits for the event on the
+ * device (no host or stream-wide synchronisation), so the storage stays
+ * bounded.  Reuse before release and double release fail explicitly.
+ * Host-side logic: slots are carved from the caller's device buffer; the only
+ * HIP calls are event create (lazily, at a slot's first release), record,
+ * stream-wait and destroy.  Not thread-safe: one ring per host thread.
+ * Graph capture: a release recorded during a capture is waited on only by
+ * acquires inside the same capture; a release recorded outside any capture
+ * is not waited on inside one (capture begins after the caller's
+ * synchronisation, so the eager warm-up has completed). */
+#define MOE_RING_MAX_SLOTS 32
+typedef struct moe_ring {
+    void* base;                                  /* caller's storage, n_slots * slot_bytes */
+    size_t slot_bytes;                           /* multiple of 256                        */
+    int32_t n_slots;                             /* 1 .. MOE_RING_MAX_SLOTS                */
+    int32_t next;                                /* next slot in rotation                  */
+    uint64_t acquisitions;
+    int32_t state[MOE_RING_MAX_SLOTS];           /* 0 free, 1 acquired                     */
+    int32_t event_kind[MOE_RING_MAX_SLOTS];      /* 0 none, 1 eager, 2 recorded in capture */
+    unsigned long long event_capture[MOE_RING_MAX_SLOTS];  /* capture id of kind 2         */
+    void* event[MOE_RING_MAX_SLOTS];             /* hipEvent_t of the last release         */
+} moe_ring;
+
+/* Set up a ring over d_base (256-byte aligned, >= n_slots * slot_bytes bytes,
+ * owned by the caller).  Host only.  MOE_ESHAPE for n_slots outside
+ * 1..MOE_RING_MAX_SLOTS or slot_bytes not a positive multiple of 256. */
+int moe_ring_init(moe_ring* r, void* d_base, size_t slot_bytes, int32_t n_slots);
+
+/* Take the next slot in rotation for a producer on `stream`: *d_slot is its
+ * device address, *slot its index.  If the slot was released before, `stream`
+ * waits (on the device) for that release.  MOE_EBUSY if the slot's previous
+ * acquisition has not been released: the ring is too small for the schedule
+ * (early reuse, [P1] "Known limitations"). */
+int moe_ring_acquire(moe_ring* r, void* stream, void** d_slot, int32_t* slot);
+
+/* The final consumer on `stream` is done with `slot` once the work enqueued on
+ * `stream` so far has run: records the slot's release event there.
+ * MOE_ESTATE if the slot is not currently acquired (double release). */
+int moe_ring_release(moe_ring* r, int32_t slot, void* stream);
+
+/* Destroy the ring's events (the caller's storage is untouched). */
+int moe_ring_destroy(moe_ring* r);
 
 #ifdef __cplusplus
 }

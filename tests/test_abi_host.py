@@ -183,6 +183,33 @@ def test_backward_argument_checks_before_launch():
     assert L.moe_combine_backward(C.byref(h), x, x, 1, x, C.c_void_p(base + 1), None) == A.MOE_EALIGN
 
 
+def test_ring_rotation_and_explicit_failures_on_the_host():
+    """Ring bookkeeping before any event exists touches no device: init
+    validation, rotation over the caller's slots, early reuse (MOE_EBUSY) and
+    release of a slot that is not acquired (MOE_ESTATE)."""
+    L = A.lib()
+    r = A.MoeRing()
+    base = 1 << 40                                  # never dereferenced
+    assert L.moe_ring_init(C.byref(r), None, 256, 2) == A.MOE_EINVAL
+    assert L.moe_ring_init(C.byref(r), C.c_void_p(base), 256, 0) == A.MOE_ESHAPE
+    assert L.moe_ring_init(C.byref(r), C.c_void_p(base), 256, A.RING_MAX_SLOTS + 1) == A.MOE_ESHAPE
+    assert L.moe_ring_init(C.byref(r), C.c_void_p(base), 100, 2) == A.MOE_ESHAPE
+    assert L.moe_ring_init(C.byref(r), C.c_void_p(base + 16), 256, 2) == A.MOE_EALIGN
+    assert L.moe_ring_init(C.byref(r), C.c_void_p(base), 4096, 3) == 0
+    assert L.moe_ring_release(C.byref(r), 0, None) == A.MOE_ESTATE      # never acquired
+    assert L.moe_ring_release(C.byref(r), 3, None) == A.MOE_EINVAL
+    got = []
+    for _ in range(3):
+        p, i = C.c_void_p(), C.c_int32()
+        assert L.moe_ring_acquire(C.byref(r), None, C.byref(p), C.byref(i)) == 0
+        got.append((i.value, p.value))
+    assert got == [(0, base), (1, base + 4096), (2, base + 8192)]
+    p, i = C.c_void_p(), C.c_int32()
+    assert L.moe_ring_acquire(C.byref(r), None, C.byref(p), C.byref(i)) == A.MOE_EBUSY   # slot 0 in use
+    assert r.acquisitions == 3
+    assert L.moe_ring_destroy(C.byref(r)) == 0
+
+
 def test_scratch_sizing():
     d = _desc(T=64, E=4, K=2, pad_multiple=1)
     rc, h, base, n, _buf = _host_handle(d)
