@@ -13,9 +13,14 @@
 //  * Work unit = (expert, 256 weight rows): for FC1 the gate and up rows of
 //    128 features, for FC2 256 output columns.  A unit takes all of the
 //    expert's token rows at once, so each weight row is streamed from HBM
-//    once per layer.  Segments of up to 256 rows take one 256-row pass;
-//    257..320 rows take two 128-row passes (the token chunk is then read
-//    twice, from L2); longer segments are cut into chunks of 320 rows.
+//    once per layer.  Segments of up to 256 rows take one 256-row pass.
+//    Segments of 257..320 rows take one pass over units of 192 weight rows
+//    (FC1: 96 features, FC2: 192 columns; 96 weight rows x up to 160 tokens
+//    per wavefront = 240 accumulation registers); FC1's blocks then hold 16
+//    features each, gate rows then up rows, so accumulators r and r+8 of a
+//    lane are the gate and up values of one feature.  Longer segments, and
+//    FC2 into the fp8 format, cut them into chunks of 320 rows taken by two
+//    128-row passes (the token chunk is then read twice, from L2).
 //  * Experts are dealt to XCDs (expert e -> XCD e mod 8; workgroup b runs on
 //    XCD b mod 8).  The 32 workgroups of an XCD walk that XCD's units in
 //    order and move through K at the same pace, so a token slice comes from
@@ -58,7 +63,8 @@ constexpr int XROWS_B = 320;           // token rows of a chunk of 128-row passe
 constexpr int W_SLOT = WROWS * CPR;    // 16-byte chunks of a weight stage
 constexpr int X_SLOT = XROWS_B * CPR;  // 16-byte chunks of a token stage
 constexpr int kNxcd = 8;
-static_assert((2 * W_SLOT + 2 * X_SLOT) * 16 + 8 * kMaxE + 64 <= 160 * 1024, "LDS budget");
+constexpr int BIG_BLOCKS = 6;           // 32-row weight blocks of a unit for 257..320-row segments
+static_assert((2 * W_SLOT + 2 * X_SLOT) * 16 + 12 * kMaxE + 64 <= 160 * 1024, "LDS budget");
 
 // Physical 16-byte slot of logical chunk `ch` of row `row` in a stage (8
 // chunks per row, 2 rows per 256-byte LDS line): the XOR spreads the 16 rows
@@ -165,7 +171,7 @@ template <int MODE, bool OUTQ, int NWB, int NXB, int NTB>
 __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, const int (&wrow)[2 * NWB],
                                      gchar* xbase, uint32_t voff, uint32_t xoff, uint32_t xoff_last, int pitch,
                                      int nk, int lane, int wave, int p, int q, int mv, uint16_t* obase, int Nout,
-                                     int ocol0, QOut qo) {
+                                     int ocol0, QOut qo, int vb) {
     constexpr int NWL = 2 * NWB;   // weight loads per thread per stage (one per block of 32 rows)
     // LDS write slot of this thread's chunk within a block (same for every block)
     const int tid = threadIdx.x;
@@ -305,7 +311,28 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
             const int tok = (q + 2 * i) * 32 + (lane & 31);
             if (tok < mv) {
                 uint16_t* orow = obase + (size_t)tok * Nout + ocol0 + (lane >> 5) * 4;
-                if (MODE == 0) {
+                if (MODE == 2) {
+                    // interleaved blocks: rows 0..15 gate, 16..31 up of 16 features;
+                    // accumulator r (gate) and r + 8 (up) hold the same feature
+#pragma unroll
+                    for (int j = 0; j < NWB; ++j) {
+                        if (p * NWB + j >= vb) continue;
+#pragma unroll
+                        for (int g = 0; g < 2; ++g) {
+                            float a[4];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const float gt = acc_read(acc[j][i][4 * g + r]);
+                                const float u = acc_read(acc[j][i][8 + 4 * g + r]);
+                                a[r] = gt / (1.f + __expf(-gt)) * u;
+                            }
+                            uint2 v;
+                            v.x = pack_bf16x2(a[0], a[1]);
+                            v.y = pack_bf16x2(a[2], a[3]);
+                            *(uint2*)(orow + j * 16 + g * 8) = v;
+                        }
+                    }
+                } else if (MODE == 0) {
                     // gate blocks 0..NWB/2-1, up blocks NWB/2..NWB-1 (same features)
 #pragma unroll
                     for (int j = 0; j < NWB / 2; ++j)
@@ -325,7 +352,8 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
                         }
                 } else {
 #pragma unroll
-                    for (int j = 0; j < NWB; ++j)
+                    for (int j = 0; j < NWB; ++j) {
+                        if (p * NWB + j >= vb) continue;
 #pragma unroll
                         for (int g4 = 0; g4 < 4; ++g4) {
                             uint2 v;
@@ -333,6 +361,7 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
                             v.y = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 2]), acc_read(acc[j][i][g4 * 4 + 3]));
                             *(uint2*)(orow + j * 32 + g4 * 8) = v;
                         }
+                    }
                 }
             }
         }
@@ -348,10 +377,14 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
 // Weight-row offsets of the pass over features/columns [f0, f0 + 32*2*NWB/(MODE==0 ? 2 : 1))
 // and token-row offsets of the chunk, then the pass itself for this
 // wavefront's token-block count.
+// MODE 2 (FC1, units of segments of 257..320 rows): each 32-row block holds
+// 16 features, rows 0..15 their gate rows and 16..31 their up rows; `vb` is
+// the number of blocks of the unit that exist (the rest re-read the last one
+// and are not stored).
 template <int MODE, bool OUTQ, int NWB, int NXB>
 __device__ __forceinline__ void run_pass(u32x4* wlds, u32x4* xlds, const char* We, const char* Xc, int Kdim,
                                          int Nout, int f0, int mv, uint16_t* ochunk, QOut qo, int lane, int p,
-                                         int q) {
+                                         int q, int vb = 2 * NWB) {
     const int tid = threadIdx.x;
     const int r8 = tid >> 3, c8 = (tid & 7) * 16;   // row within a 32-row block, byte offset of the chunk
     // first weight row of each 32-row block of the pass (blocks never straddle
@@ -360,17 +393,22 @@ __device__ __forceinline__ void run_pass(u32x4* wlds, u32x4* xlds, const char* W
 #pragma unroll
     for (int b = 0; b < 2 * NWB; ++b) {
         const int r = b * 32;
+        const int bv = b < vb ? b : vb - 1;
         if (MODE == 0) {
             // wavefront p: NWB/2 gate blocks then NWB/2 up blocks of features
             // f0 + p*16*NWB .. +16*NWB-1
             const int pp = r / (32 * NWB), rr = r % (32 * NWB), half = 16 * NWB;
             wrow[b] = rr < half ? f0 + pp * half + rr : Nout + f0 + pp * half + rr - half;
+        } else if (MODE == 2) {
+            wrow[b] = f0 + 16 * bv;          // first feature of the block (gate row; up rows via voff)
         } else {
-            wrow[b] = f0 + r;
+            wrow[b] = f0 + 32 * bv;
         }
     }
     const int pitch = Kdim * 2;
-    const uint32_t voff = (uint32_t)r8 * (uint32_t)pitch + (uint32_t)c8;
+    // MODE 2: rows 16..31 of a block are the up rows, Nout rows further on
+    const uint32_t vrow = MODE == 2 && r8 >= 16 ? (uint32_t)(r8 + Nout - 16) : (uint32_t)r8;
+    const uint32_t voff = vrow * (uint32_t)pitch + (uint32_t)c8;
     // token DMA lane: row 8*wave + lane/8 of a block, logical chunk of its swizzled slot
     const int wave = tid >> 6, lane8 = (tid & 63) >> 3;
     const int xr = 8 * wave + lane8;
@@ -378,15 +416,15 @@ __device__ __forceinline__ void run_pass(u32x4* wlds, u32x4* xlds, const char* W
     const uint32_t xoff = (uint32_t)xr * (uint32_t)pitch + (uint32_t)xch * 16u;
     const uint32_t xoff_last = (uint32_t)min(xr, mv - 1 - (NXB - 1) * 32) * (uint32_t)pitch + (uint32_t)xch * 16u;
     const int nk = Kdim / BK;
-    const int ocol0 = MODE == 0 ? f0 + p * 16 * NWB : f0 + p * 32 * NWB;
+    const int ocol0 = MODE != 1 ? f0 + p * 16 * NWB : f0 + p * 32 * NWB;
     if (q == 0)
         pass<MODE, OUTQ, NWB, NXB, (NXB + 1) / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff,
                                                   xoff_last, pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p,
-                                                  q, mv, ochunk, Nout, ocol0, qo);
+                                                  q, mv, ochunk, Nout, ocol0, qo, vb);
     else
         pass<MODE, OUTQ, NWB, NXB, NXB / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff,
                                             xoff_last, pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p, q,
-                                            mv, ochunk, Nout, ocol0, qo);
+                                            mv, ochunk, Nout, ocol0, qo, vb);
 }
 
 // ---- 128-row passes (segments of 257..320 rows) ------------------------------
@@ -643,10 +681,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Out,
     uint8_t* __restrict__ Oq, float* __restrict__ Os, const int64_t* __restrict__ seg_off,
     const int32_t* __restrict__ kept, int E, long long R, int Kdim, int Wrows, int Nout, int n_units) {
+    // units of segments of 257..320 rows: BIG_BLOCKS blocks of 16 features (FC1) / 32 columns (FC2)
+    const int n_big = MODE == 0 ? (Nout / 16 + BIG_BLOCKS - 1) / BIG_BLOCKS : (Nout / 32 + BIG_BLOCKS - 1) / BIG_BLOCKS;
     __shared__ u32x4 wlds[2 * W_SLOT];
     __shared__ u32x4 xlds[2 * X_SLOT];
     __shared__ int s_list[kMaxE];      // active experts of this XCD, ascending
     __shared__ int s_rows[kMaxE];      // their row counts (clipped to R)
+    __shared__ int s_pref[kMaxE + 1];  // first work item of each of them
     __shared__ int s_cnt;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -676,15 +717,44 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             }
             run += __popcll(act);
         }
-        if (lane == 0) s_cnt = run;
+        if (lane == 0) {
+            // segments of 257..320 rows take BIG_BLOCKS-block units (one pass)
+            int acc_u = 0;
+            for (int i = 0; i < run; ++i) {
+                s_pref[i] = acc_u;
+                acc_u += (!OUTQ && s_rows[i] > XROWS_A && s_rows[i] <= XROWS_B) ? n_big : n_units;
+            }
+            s_pref[run] = acc_u;
+            s_cnt = run;
+        }
     }
     __syncthreads();
-    const int total = s_cnt * n_units;
+    const int total = s_pref[s_cnt];
 
     for (int t = j; t < total; t += P) {
-        const int slot = t / n_units, nt = t - slot * n_units;
+        int lo = 0, hi = s_cnt - 1;          // last slot whose first item is <= t
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pref[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        const int slot = lo, nt = t - s_pref[slot];
         const int e = s_list[slot];
         const int me = s_rows[slot];
+        if (!OUTQ && me > XROWS_A && me <= XROWS_B) {
+            // one pass over all rows: 96 features (FC1) / 192 columns (FC2) per unit
+            const char* We = (const char*)(W + (size_t)e * Wrows * Kdim);
+            const char* Xc = (const char*)(X + (size_t)seg_off[e] * Kdim);
+            uint16_t* oc = Out + (size_t)seg_off[e] * Nout;
+            const int bsz = MODE == 0 ? 16 : 32;                  // features (FC1) / columns (FC2) per block
+            const int f0 = nt * BIG_BLOCKS * bsz;
+            const int vb = min(BIG_BLOCKS, Nout / bsz - nt * BIG_BLOCKS);
+            const QOut qn = {nullptr, nullptr};
+            if ((me + 31) / 32 == 9)
+                run_pass<MODE == 0 ? 2 : 1, false, 3, 9>(wlds, xlds, We, Xc, Kdim, Nout, f0, me, oc, qn, lane, p, q, vb);
+            else
+                run_pass<MODE == 0 ? 2 : 1, false, 3, 10>(wlds, xlds, We, Xc, Kdim, Nout, f0, me, oc, qn, lane, p, q, vb);
+            continue;
+        }
         const long long seg = seg_off[e];
         const char* We = (const char*)(W + (size_t)e * Wrows * Kdim);
         const int u0 = nt * (MODE == 0 ? 128 : 256);    // first feature (FC1) / output column (FC2) of the unit
