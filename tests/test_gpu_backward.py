@@ -154,3 +154,53 @@ def test_backward_full_size_sampled():
                          S.bf16_to_float(Y_s).astype(np.float64), c.H)
     gq_s = gq.cpu().numpy()[sample].astype(np.float64)
     assert np.all(np.abs(gq_s - wq) <= tol + 2.0 ** -24 * np.abs(wq))
+
+
+def test_backward_graph_replay_matches_eager():
+    """dispatch_backward + combine_backward (Boolean-map routing, so the
+    probability tables are cleared by the fill kernel) captured in one HIP
+    graph and replayed with new gradients, each replay checked against the
+    eager result."""
+    T, H, E, K = 300, 1024, 16, 4
+    routing, probs = _routing(T, E, K, oracle.FMT_SPARSE_U8, 91)
+    d = Dispatcher(T, H, E, K, route_fmt="sparse_bool", pad_multiple=8)
+    d.preprocess(dev(routing), dev(probs))
+    G = torch.empty((d.R, H), dtype=torch.bfloat16, device=DEV)
+    Y = dev(S.bf16_normal((d.R, H), 92))
+    gy = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    gop = torch.empty(d.R, dtype=torch.float32, device=DEV)
+    gx = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    gp = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    gY = torch.empty((d.R, H), dtype=torch.bfloat16, device=DEV)
+    gq = torch.empty((T, E), dtype=torch.float32, device=DEV)
+
+    def step():
+        d.dispatch_backward(G, gop, out=gx, grad_probs=gp)
+        d.combine_backward(gy, Y, True, out=gY, grad_probs=gq)
+
+    def fill(i):
+        G.copy_(dev(S.bf16_normal((d.R, H), 100 + i)))
+        gy.copy_(dev(S.bf16_normal((T, H), 200 + i)))
+        gop.copy_(torch.from_numpy(np.random.default_rng(300 + i).standard_normal(d.R).astype(np.float32)))
+
+    log("backward graph replay")
+    fill(0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    rows = d.src_row >= 0
+    for i in range(1, 4):
+        fill(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (gx.clone(), gp.clone(), gY[rows].clone(), gq.clone())
+        step()                                        # eager on the same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], gx) and torch.equal(got[1], gp), i
+        assert torch.equal(got[2], gY[rows]) and torch.equal(got[3], gq), i

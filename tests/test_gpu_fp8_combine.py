@@ -130,3 +130,54 @@ def test_fp8_combine_format_full_size_sampled():
     g = host_bf16(y)[sample]
     assert row_rel_l2(S.bf16_to_float(g), S.bf16_to_float(want)).max() < 1e-2
     assert np.mean(g == want) > 0.99
+
+
+def test_fp8_formats_graph_replay_matches_eager():
+    """Quantise-on-dispatch, FC2 into the fp8 format and the fp8 combine (and
+    the bf16 FC1 between them) captured in one graph; every replay with new
+    tokens equals the eager result."""
+    c, idx, pr, x, w1, w2 = _small_layer()
+    W1, W2 = dev(w1), dev(w2)
+    d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)
+    dq = Dispatcher(c.T, c.H, c.E, c.K, payload="fp8", pad_multiple=c.pad)
+    rt, pt = dev(idx), dev(pr)
+    d.preprocess(rt, pt)
+    dq.preprocess(rt, pt)
+    xt = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+    perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+    pq = torch.empty((dq.R, c.H), dtype=torch.uint8, device=DEV)
+    ps = torch.empty((dq.R, c.H // 128), dtype=torch.float32, device=DEV)
+    scr = d.alloc_mlp_scratch(c.F)
+    eq = torch.empty((d.R, c.H), dtype=torch.uint8, device=DEV)
+    es = torch.empty((d.R, c.H // 128), dtype=torch.float32, device=DEV)
+    y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        dq.permute_quantize(xt, out=pq, out_scales=ps)
+        d.permute(xt, out=perm)
+        d.fc1(perm, W1, scr)
+        d.fc2_fp8out(W2, scr, out=eq, out_scales=es)
+        d.combine_fp8(eq, es, out=y)
+
+    log("fp8 formats graph replay")
+    xt.copy_(dev(x))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    rows = d.src_row >= 0
+    for i in range(1, 4):
+        xt.copy_(dev(S.bf16_normal((c.T, c.H), 400 + i)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (pq[rows].clone(), ps[rows].clone(), eq[rows].clone(), es[rows].clone(), y.clone())
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], pq[rows]) and torch.equal(got[1], ps[rows]), i
+        assert torch.equal(got[2], eq[rows]) and torch.equal(got[3], es[rows]), i
+        assert torch.equal(got[4], y), i
