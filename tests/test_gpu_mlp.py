@@ -54,6 +54,57 @@ def test_grouped_mlp_ragged_groups(counts, H, F, pad):
         _check_rows(got[s:s + k], want, f"expert {e}")
 
 
+@pytest.mark.parametrize("fp8_out", [False, True])
+def test_grouped_mlp_unit_chains(fp8_out):
+    """64 experts of 97..420 rows (every pass shape: 256-row passes over 4..8
+    token blocks, 192-row units over 9..10 blocks, chunks of 320 rows plus a
+    rest), H = F = 2048: each workgroup takes several units of different
+    shapes in a row, reusing its LDS rings across them.  Sampled rows of every
+    expert (first, last and random ones; each row spans every unit of its
+    expert) against the oracle; with fp8_out, FC2 writes the fp8 combine
+    format, checked against the oracle's quantiser on its float32 FC2 sums."""
+    E, H, F = 64, 2048, 2048
+    rng = np.random.default_rng(64)
+    counts = rng.integers(97, 321, E)
+    counts[::9] = rng.integers(321, 421, len(counts[::9]))
+    T = int(counts.sum())
+    idx = np.repeat(np.arange(E), counts).astype(np.int16)[:, None]
+    idx = idx[rng.permutation(T)]
+    x = S.bf16_normal((T, H), 65)
+    w1 = S.weights_bf16(E, 2 * F, H, 66, std=0.05, device=DEV)
+    w2 = S.weights_bf16(E, H, F, 67, std=0.05, device=DEV)
+    log("mlp unit chains", T, E, H, F, "fp8_out" if fp8_out else "bf16_out")
+    d = Dispatcher(T, H, E, 1, pad_multiple=1)
+    perm, *_ = d.dispatch(dev(x), dev(idx))
+    scratch = d.alloc_mlp_scratch(F)
+    d.fc1(perm, w1, scratch)
+    if fp8_out:
+        yq, ys = d.fc2_fp8out(w2, scratch)
+    else:
+        y = d.fc2(w2, scratch, torch.empty((d.R, H), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    rt = oracle.route(idx, 0, E, 1, None, 1, -1, d.R)
+    assert np.array_equal(d.row_id.cpu().numpy(), rt["row_id"])
+    P = oracle.permute_rows(x, rt["row_id"], d.R)
+    for e in range(E):
+        s, k = int(rt["seg_off"][e]), int(rt["counts"][e])
+        rows = np.unique(np.concatenate([[0, k - 1], rng.integers(0, k, 3)]))
+        sel = torch.from_numpy(s + rows).to(DEV)
+        if fp8_out:
+            # against the oracle's quantiser on its float32 FC2 sums (the bar of
+            # the fp8 combine format: scales and dequantised rows within 1e-2)
+            _, y32 = oracle.expert_mlp_bf16(P[s + rows], host_bf16(w1[e]), host_bf16(w2[e]), return_y32=True)
+            wq, ws = oracle.quant_rows_e4m3(y32)
+            gq, gs = yq[sel].cpu().numpy(), ys[sel].cpu().numpy()
+            g = torch.from_numpy(gq).view(torch.float8_e4m3fn).double().numpy() * np.repeat(gs, 128, axis=1)
+            w = torch.from_numpy(wq).view(torch.float8_e4m3fn).double().numpy() * np.repeat(ws, 128, axis=1)
+            assert np.all(np.abs(gs / ws - 1.0) <= 1e-2), e
+            assert rel_l2(g, w) < TOL and row_rel_l2(g, w).max() < 5e-2, (e, k, rel_l2(g, w))
+        else:
+            want = oracle.expert_mlp_bf16(P[s + rows], host_bf16(w1[e]), host_bf16(w2[e]))
+            _check_rows(host_bf16(y[sel]), want, f"expert {e} ({k} rows)")
+
+
 def test_mlp_zero_weights_give_zero():
     T, H, E, F = 200, 256, 4, 128
     idx = np.random.default_rng(1).integers(0, E, (T, 2)).astype(np.int16)
