@@ -15,6 +15,8 @@
 //     expert and popcount(mask & lanes_below) is a token's stable rank inside
 //     the tile, so ranks are deterministic without ordered atomics.  It also
 //     writes each slot's expert id (or -1) and probability, and tile flags.
+//     Boolean maps take k_route_tiles_sparse: four wavefronts per tile, each
+//     over a quarter of the experts, joined by a scan of per-token counts.
 //  2. k_route_scan   -- one 1024-thread workgroup: per-expert exclusive scan
 //     of tile counts, raw counts, capacity, padding, exclusive scan over
 //     experts, rows needed, flag word.
@@ -44,7 +46,8 @@ __global__ __launch_bounds__(64) void k_route_tiles(const void* __restrict__ rou
     int err = 0;
     const bool in = t < T;
     const bool live = t < T_live;
-    if (FMT != MOE_ROUTE_SPARSE_BOOL) {
+    static_assert(FMT != MOE_ROUTE_SPARSE_BOOL, "Boolean maps take k_route_tiles_sparse");
+    {
         if (in) {
             const unsigned long long bit = 1ull << lane;
             for (int j = 0; j < K; ++j) {
@@ -73,56 +76,102 @@ __global__ __launch_bounds__(64) void k_route_tiles(const void* __restrict__ rou
                 copy_prob[at] = p;
             }
         }
-    } else {
-        // Boolean map: walk experts in ascending order (wave-uniform loop);
-        // the j-th routed expert of a row fills slot j.
-        int j = 0;
-        const uint8_t* row = (const uint8_t*)routing + (size_t)(live ? t : 0) * E;
-        const bool vec = (E % 16) == 0;
-        for (int e0 = 0; e0 < E; e0 += 16) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (live) {
-                if (vec) {
-                    v = *(const u32x4*)(row + e0);
-                } else {
-                    uint32_t w[4] = {0u, 0u, 0u, 0u};
-                    for (int i = 0; i < 16 && e0 + i < E; ++i) w[i >> 2] |= (uint32_t)(row[e0 + i] != 0) << ((i & 3) * 8);
-                    v = u32x4{w[0], w[1], w[2], w[3]};
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int e = e0 + i;
-                const bool r = e < E && ((v[i >> 2] >> ((i & 3) * 8)) & 0xffu) != 0u;
-                bool sel = false;
-                if (r) {
-                    if (j < K) {
-                        const size_t at = (size_t)t * K + j;
-                        row_id[at] = e;
-                        copy_prob[at] = probs ? probs[(size_t)t * E + e] : 1.f;
-                        ++j;
-                        sel = true;
-                    } else {
-                        err |= MOE_FLAG_DUPLICATE;
-                    }
-                }
-                const unsigned long long b = __ballot(sel);
-                if (lane == 0 && e < E) msk[e] = b;
-            }
-        }
-        if (in) {
-            for (; j < K; ++j) {
-                const size_t at = (size_t)t * K + j;
-                row_id[at] = -1;
-                copy_prob[at] = 0.f;
-            }
-        }
     }
     __syncthreads();
     for (int e = lane; e < E; e += 64) tile_mask[(size_t)tile * E + e] = msk[e];
     const unsigned long long bad = __ballot((err & MOE_FLAG_BAD_EXPERT) != 0);
     const unsigned long long dup = __ballot((err & MOE_FLAG_DUPLICATE) != 0);
     if (lane == 0) tile_err[tile] = (bad ? MOE_FLAG_BAD_EXPERT : 0) | (dup ? MOE_FLAG_DUPLICATE : 0);
+}
+
+// Boolean map [T,E]: one workgroup of four wavefronts per 64-token tile.
+// Wavefront w walks experts [w*Eq, (w+1)*Eq) (Eq = E/4 rounded up to 16) in
+// ascending order.  A token's routed experts fill its slots in ascending
+// expert order, so wavefront w's first slot for a token is the number of that
+// token's routed experts below its range: a scan over the four wavefronts'
+// per-token counts.  Slots past K are not written (duplicate bit); the
+// wavefront owning the top of the range clears the token's unused slots.
+__global__ __launch_bounds__(256) void k_route_tiles_sparse(const uint8_t* __restrict__ routing,
+                                                            const float* __restrict__ probs,
+                                                            const int32_t* __restrict__ T_live_ptr, int T, int E,
+                                                            int K, uint64_t* __restrict__ tile_mask,
+                                                            int32_t* __restrict__ tile_err,
+                                                            int32_t* __restrict__ row_id,
+                                                            float* __restrict__ copy_prob) {
+    __shared__ unsigned long long msk[kMaxE];
+    __shared__ int cnt[4][kTileTok];
+    __shared__ int serr;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tile = blockIdx.x;
+    const int t = tile * kTileTok + lane;
+    int T_live = T;
+    if (T_live_ptr) T_live = min(max(*T_live_ptr, 0), T);
+    const bool in = t < T;
+    const bool live = t < T_live;
+    const int Eq = ((E + 3) / 4 + 15) / 16 * 16;
+    const int eb = min(E, w * Eq), ee = min(E, eb + Eq);
+    const uint8_t* row = routing + (size_t)(live ? t : 0) * E;
+    const bool vec = (E % 16) == 0;   // then every range is whole 16-byte chunks
+    // routed flags of experts e0..e0+15 (byte i of the chunk; 0 past the range)
+    auto chunk = [&](int e0) -> u32x4 {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (live) {
+            if (vec) {
+                v = *(const u32x4*)(row + e0);
+            } else {
+                uint32_t x[4] = {0u, 0u, 0u, 0u};
+                for (int i = 0; i < 16 && e0 + i < ee; ++i) x[i >> 2] |= (uint32_t)(row[e0 + i] != 0) << ((i & 3) * 8);
+                v = u32x4{x[0], x[1], x[2], x[3]};
+            }
+        }
+        return v;
+    };
+    auto routed = [](const u32x4& v, int i) { return ((v[i >> 2] >> ((i & 3) * 8)) & 0xffu) != 0u; };
+
+    int c = 0;
+    for (int e0 = eb; e0 < ee; e0 += 16) {
+        const u32x4 v = chunk(e0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c += (e0 + i < ee && routed(v, i)) ? 1 : 0;
+    }
+    cnt[w][lane] = c;
+    if (threadIdx.x == 0) serr = 0;
+    __syncthreads();
+    int j = 0;
+    for (int w2 = 0; w2 < w; ++w2) j += cnt[w2][lane];
+    int err = 0;
+    for (int e0 = eb; e0 < ee; e0 += 16) {
+        const u32x4 v = chunk(e0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = e0 + i;
+            bool sel = false;
+            if (e < ee && routed(v, i)) {
+                if (j < K) {
+                    const size_t at = (size_t)t * K + j;
+                    row_id[at] = e;
+                    copy_prob[at] = probs ? probs[(size_t)t * E + e] : 1.f;
+                    ++j;
+                    sel = true;
+                } else {
+                    err |= MOE_FLAG_DUPLICATE;
+                }
+            }
+            const unsigned long long b = __ballot(sel);
+            if (lane == 0 && e < ee) msk[e] = b;
+        }
+    }
+    if (w == 3 && in) {
+        for (; j < K; ++j) {
+            const size_t at = (size_t)t * K + j;
+            row_id[at] = -1;
+            copy_prob[at] = 0.f;
+        }
+    }
+    if (err) atomicOr(&serr, err);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) tile_mask[(size_t)tile * E + e] = msk[e];
+    if (threadIdx.x == 0) tile_err[tile] = serr;
 }
 
 __global__ __launch_bounds__(1024) void k_route_scan(
@@ -265,7 +314,7 @@ hipError_t launch_route(const moe_handle* h, const void* routing, const float* p
                                    T_live, d.T, d.E, d.K, h->tile_mask, h->tile_err, h->row_id, h->copy_prob);
                 break;
             default:
-                hipLaunchKernelGGL(k_route_tiles<MOE_ROUTE_SPARSE_BOOL>, dim3(nt), dim3(64), 0, s, routing, probs,
+                hipLaunchKernelGGL(k_route_tiles_sparse, dim3(nt), dim3(256), 0, s, (const uint8_t*)routing, probs,
                                    T_live, d.T, d.E, d.K, h->tile_mask, h->tile_err, h->row_id, h->copy_prob);
                 break;
         }
