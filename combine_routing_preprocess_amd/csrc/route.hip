@@ -195,16 +195,37 @@ __global__ __launch_bounds__(1024) void k_route_scan(
     const int g = tid / E, e = tid - g * E;
     const bool act = tid < S * E;
     const int t0 = g * chunk, t1 = min(n_tiles, t0 + chunk);
+    // tile masks are read eight tiles at a time, so their loads overlap
+    constexpr int U = 8;
     int sum = 0;
     if (act) {
-        for (int tl = t0; tl < t1; ++tl) sum += __popcll(tile_mask[(size_t)tl * E + e]);
+        int tl = t0;
+        for (; tl + U <= t1; tl += U) {
+            unsigned long long m[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) m[u] = tile_mask[(size_t)(tl + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum += __popcll(m[u]);
+        }
+        for (; tl < t1; ++tl) sum += __popcll(tile_mask[(size_t)tl * E + e]);
         part[g * E + e] = sum;
     }
     __syncthreads();
     if (act) {
         int run = 0;
         for (int g2 = 0; g2 < g; ++g2) run += part[g2 * E + e];
-        for (int tl = t0; tl < t1; ++tl) {
+        int tl = t0;
+        for (; tl + U <= t1; tl += U) {
+            unsigned long long m[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) m[u] = tile_mask[(size_t)(tl + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                tile_base[(size_t)(tl + u) * E + e] = run;
+                run += __popcll(m[u]);
+            }
+        }
+        for (; tl < t1; ++tl) {
             tile_base[(size_t)tl * E + e] = run;
             run += __popcll(tile_mask[(size_t)tl * E + e]);
         }
@@ -253,20 +274,39 @@ __global__ __launch_bounds__(256) void k_route_assign(
         const int t = tile * kTileTok + lane;
         if (t >= T) return;
         const unsigned long long below = (1ull << lane) - 1ull;
-        for (int j = 0; j < K; ++j) {
-            const size_t at = (size_t)t * K + j;
-            const int e = row_id[at];
-            if (e < 0) continue;
-            const size_t te = (size_t)tile * E + e;
-            const int rank = tile_base[te] + __popcll(tile_mask[te] & below);
-            const long long row = seg_off[e] + rank;
-            if (rank < kept[e] && row < R) {
-                row_id[at] = (int)row;
-                src_row[row] = t;
-                if (out_probs) out_probs[row] = copy_prob[at];
-            } else {
-                row_id[at] = -1;
-                copy_prob[at] = 0.f;
+        // slots are taken eight at a time: their expert ids, then all the
+        // per-expert lookups, are loaded together so their latencies overlap
+        constexpr int U = 8;
+        for (int j0 = 0; j0 < K; j0 += U) {
+            int e[U], tb[U], kp[U];
+            unsigned long long tm[U];
+            long long so[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) e[u] = j0 + u < K ? row_id[(size_t)t * K + j0 + u] : -1;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (e[u] >= 0) {
+                    const size_t te = (size_t)tile * E + e[u];
+                    tb[u] = tile_base[te];
+                    tm[u] = tile_mask[te];
+                    so[u] = seg_off[e[u]];
+                    kp[u] = kept[e[u]];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (e[u] < 0) continue;
+                const size_t at = (size_t)t * K + j0 + u;
+                const int rank = tb[u] + __popcll(tm[u] & below);
+                const long long row = so[u] + rank;
+                if (rank < kp[u] && row < R) {
+                    row_id[at] = (int)row;
+                    src_row[row] = t;
+                    if (out_probs) out_probs[row] = copy_prob[at];
+                } else {
+                    row_id[at] = -1;
+                    copy_prob[at] = 0.f;
+                }
             }
         }
         return;
