@@ -180,7 +180,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(
     int32_t* __restrict__ kept_out, int64_t* __restrict__ seg_off, int64_t* __restrict__ rows_needed,
     int32_t* __restrict__ flag) {
     __shared__ int part[1024];
-    __shared__ long long scan[1024];
+    __shared__ long long scan[16];     // wavefront totals of the expert scan
     __shared__ int sflag;
     const int tid = threadIdx.x;
     int S = 1;
@@ -243,19 +243,25 @@ __global__ __launch_bounds__(1024) void k_route_scan(
         kept_out[tid] = kept;
         padded = ((long long)kept + pad - 1) / pad * pad;
     }
-    scan[tid] = padded;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const long long v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
+    // inclusive scan over experts: within each wavefront by shuffles, then
+    // the wavefront totals (16 of them) in LDS
+    const int lane = tid & 63, wv = tid >> 6;
+    long long incl = padded;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const long long v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
     }
-    if (tid < E) seg_off[tid] = scan[tid] - padded;
+    if (lane == 63) scan[wv] = incl;
+    __syncthreads();
+    long long before = 0;
+    for (int w2 = 0; w2 < wv; ++w2) before += scan[w2];
+    incl += before;
+    if (tid < E) seg_off[tid] = incl - padded;
     if (tid == E - 1) {
-        seg_off[E] = scan[tid];
-        *rows_needed = scan[tid];
-        if (scan[tid] > R) atomicOr(&sflag, MOE_FLAG_OUT_ROWS);
+        seg_off[E] = incl;
+        *rows_needed = incl;
+        if (incl > R) atomicOr(&sflag, MOE_FLAG_OUT_ROWS);
     }
     __syncthreads();
     if (tid == 0) *flag = sflag;
