@@ -70,7 +70,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the single-GPU layer: every expert is local to one MI355X and there is no "
-              "cross-GPU exchange in this build, so --gpus must be 1.", file=sys.stderr)
+              "cross-GPU exchange in this library, so --gpus must be 1.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -85,7 +85,7 @@ def main() -> int:
     dev = "cuda"
     if args.workload == "decode":
         return run_decode(args)
-    c = S.CONFIGS["cfg4_dsv3_layer"]
+    c = S.CONFIGS["dsv3_layer_8192x7168_e256"]
     T, H, E, K, F, pad = c.T, c.H, c.E, c.K, c.F, c.pad
 
     # ---- inputs, resident in HBM -------------------------------------------
@@ -340,7 +340,7 @@ def run_decode(args):
     import moe_synth as S
     from combine_routing_preprocess_amd import Dispatcher
     dev = "cuda"
-    c = S.CONFIGS["cfg5_decode_fp8"]
+    c = S.CONFIGS["decode_fp8_7168_e256"]
     T_live = args.tokens
     T = S.next_pow2_bucket(T_live)
     log(f"drawing fp8 weights; {T_live} live tokens in bucket {T}")
@@ -395,7 +395,7 @@ def run_extra(args):
     del a, b
 
     # permute + combine, 8192 x 7168 bf16, 32 experts top-8, capacity 1.5x
-    c = S.CONFIGS["cfg2_permute_combine"]
+    c = S.CONFIGS["permute_combine_8192x7168_e32"]
     idx, pr = S.route_uniform_distinct(c.T, c.E, c.K, c.seed)
     mx = int(oracle.route(idx, 0, c.E, c.K, pr)["counts"].max())
     cap = oracle.capacity_from_rows(mx, 1.5)
@@ -411,7 +411,7 @@ def run_extra(args):
     pw, _ = _event_times(lambda: d.permute(x, out=perm))
     cw, _ = _event_times(lambda: d.combine(perm, out=y))
     gm, gmed = _graph_times(lambda: (d.dispatch(x, rt, pt, out=perm), d.combine(perm, out=y)))
-    res["cfg2_permute_combine"] = {
+    res["permute_combine_8192x7168_e32"] = {
         "capacity": cap, "timing": "cold caches (512 MB copy before each run); warm = repeated runs",
         "permute_min_ms": round(pm, 4), "combine_min_ms": round(cm, 4),
         "permute_GB_s": round(nbytes / (pm * 1e-3) / 1e9, 1), "combine_GB_s": round(nbytes / (cm * 1e-3) / 1e9, 1),
@@ -422,7 +422,7 @@ def run_extra(args):
 
     # backward of dispatch and combine at the layer shape (8192 x 7168, 256
     # experts top-8, padding 128), cold caches
-    c = S.CONFIGS["cfg4_dsv3_layer"]
+    c = S.CONFIGS["dsv3_layer_8192x7168_e256"]
     idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
     d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)
     d.preprocess(torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev))
@@ -451,7 +451,7 @@ def run_extra(args):
 
     # fp8 formats at the layer shape: quantise-on-dispatch, FC2 into the fp8
     # combine format and the fp8 combine, against their bf16 counterparts
-    c = S.CONFIGS["cfg4_dsv3_layer"]
+    c = S.CONFIGS["dsv3_layer_8192x7168_e256"]
     idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
     rt, pt = torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev)
     x = torch.from_numpy(S.bf16_normal((c.T, c.H), c.seed).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -506,7 +506,7 @@ def run_extra(args):
     del dq, pq, ps, d, perm, scr, eo, eq, es, y, w1, w2, x
 
     # routing stress: 256 experts top-36 Zipf, fp8 payload, dense vs Boolean map
-    c = S.CONFIGS["cfg3_route_stress_fp8"]
+    c = S.CONFIGS["route_stress_fp8_8192x7168_e256"]
     idx, _ = S.route_zipf_gumbel(c.T, c.E, c.K, c.seed)
     m, _ = S.dense_to_sparse(idx, c.E)
     xq, xs = S.quantize_rows_fp8_torch(S.bf16_normal((c.T, c.H), c.seed))
@@ -523,10 +523,10 @@ def run_extra(args):
         out3[name] = {"preprocess_min_us": round(km * 1e3, 1), "permute_min_ms": round(pmn, 4),
                       "permute_GB_s": round(nb / (pmn * 1e-3) / 1e9, 1)}
         del d, po, so
-    res["cfg3_route_stress_fp8"] = out3
+    res["route_stress_fp8_8192x7168_e256"] = out3
 
     # decode buckets, fp8 weights, graph replay of dispatch + FC1 + FC2 + combine
-    c = S.CONFIGS["cfg5_decode_fp8"]
+    c = S.CONFIGS["decode_fp8_7168_e256"]
     w1q, w1s = S.weights_fp8_blocks(c.E, 2 * c.F, c.H, c.seed + 1, device=dev)
     w2q, w2s = S.weights_fp8_blocks(c.E, c.H, c.F, c.seed + 2, device=dev)
     per_expert = (2 * c.F * c.H + c.H * c.F) + 4 * (2 * c.F // 128 * c.H // 128 + c.H // 128 * c.F // 128)
@@ -571,7 +571,7 @@ def run_extra(args):
                                                   "tokens_per_s": round(T / (qm * 1e-3), 1),
                                                   "same_output": same}}
         del d, perm, scr, eo, y, dq, pq, ps, scq, eq, yq
-    res["cfg5_decode_fp8"] = out5
+    res["decode_fp8_7168_e256"] = out5
     return res
 
 

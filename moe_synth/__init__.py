@@ -57,11 +57,11 @@ class Config:
 
 # The five synthetic workloads.  ``seed`` is 1000 + index.
 CONFIGS = {
-    "cfg1_small_layer": Config("cfg1_small_layer", T=512, H=1024, E=16, K=4, F=512, pad=32, seed=1001),
-    "cfg2_permute_combine": Config("cfg2_permute_combine", T=8192, H=7168, E=32, K=8, F=0, pad=1, seed=1002),
-    "cfg3_route_stress_fp8": Config("cfg3_route_stress_fp8", T=8192, H=7168, E=256, K=36, F=0, pad=1, seed=1003),
-    "cfg4_dsv3_layer": Config("cfg4_dsv3_layer", T=8192, H=7168, E=256, K=8, F=2048, pad=128, seed=1004),
-    "cfg5_decode_fp8": Config("cfg5_decode_fp8", T=256, H=7168, E=256, K=8, F=2048, pad=16, seed=1005),
+    "small_layer_512x1024": Config("small_layer_512x1024", T=512, H=1024, E=16, K=4, F=512, pad=32, seed=1001),
+    "permute_combine_8192x7168_e32": Config("permute_combine_8192x7168_e32", T=8192, H=7168, E=32, K=8, F=0, pad=1, seed=1002),
+    "route_stress_fp8_8192x7168_e256": Config("route_stress_fp8_8192x7168_e256", T=8192, H=7168, E=256, K=36, F=0, pad=1, seed=1003),
+    "dsv3_layer_8192x7168_e256": Config("dsv3_layer_8192x7168_e256", T=8192, H=7168, E=256, K=8, F=2048, pad=128, seed=1004),
+    "decode_fp8_7168_e256": Config("decode_fp8_7168_e256", T=256, H=7168, E=256, K=8, F=2048, pad=16, seed=1005),
 }
 
 

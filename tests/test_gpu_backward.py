@@ -111,7 +111,7 @@ def test_backward_full_size_sampled():
     """8192 x 7168 bf16, 256 experts top-8 sigmoid routing, padding 128: the
     whole backward runs at full size; sampled tokens are checked against the
     oracle on the rows they touch."""
-    c = S.CONFIGS["cfg4_dsv3_layer"]
+    c = S.CONFIGS["dsv3_layer_8192x7168_e256"]
     idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
     log("backward full size")
     d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)

@@ -23,7 +23,7 @@ def _deq(q, s):
 
 
 def _small_layer():
-    c = S.CONFIGS["cfg1_small_layer"]
+    c = S.CONFIGS["small_layer_512x1024"]
     idx, pr = S.route_softmax_topk(c.T, c.E, c.K, c.seed)
     x = S.bf16_normal((c.T, c.H), c.seed)
     w1 = S.bf16_normal((c.E, 2 * c.F, c.H), c.seed + 1, std=0.02)
@@ -98,7 +98,7 @@ def test_fp8_combine_format_full_size_sampled():
     """8192 x 7168, 256 experts top-8, FFN 2048: FC2 into the fp8 format
     agrees with FC2's bf16 output up to fp8 rounding at full size, and the
     combine of sampled tokens matches the oracle on the GPU's codes."""
-    c = S.CONFIGS["cfg4_dsv3_layer"]
+    c = S.CONFIGS["dsv3_layer_8192x7168_e256"]
     idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
     x = torch.from_numpy(S.bf16_normal((c.T, c.H), c.seed).view(np.int16)).to(DEV).view(torch.bfloat16)
     w1 = S.weights_bf16(c.E, 2 * c.F, c.H, c.seed + 1, device=DEV)

@@ -54,7 +54,7 @@ def test_fp8_mlp_ragged(counts, H, F):
 def fp8_weights():
     """256 experts, H 7168, FFN 2048, e4m3 weights drawn N(0, 0.02) with
     128x128 block scales (W1 7.5 GB + W2 3.8 GB on the device)."""
-    c = S.CONFIGS["cfg5_decode_fp8"]
+    c = S.CONFIGS["decode_fp8_7168_e256"]
     w1q, w1s = S.weights_fp8_blocks(c.E, 2 * c.F, c.H, c.seed + 1, device=DEV)
     w2q, w2s = S.weights_fp8_blocks(c.E, c.H, c.F, c.seed + 2, device=DEV)
     yield c, w1q, w1s, w2q, w2s

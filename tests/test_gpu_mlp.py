@@ -123,19 +123,19 @@ def test_mlp_zero_weights_give_zero():
 def test_small_layer_full_parity():
     """512 tokens x 1024, 16 experts top-4 (softmax), padding 32, FFN 512:
     every output token against the oracle layer."""
-    c = S.CONFIGS["cfg1_small_layer"]
+    c = S.CONFIGS["small_layer_512x1024"]
     idx, pr = S.route_softmax_topk(c.T, c.E, c.K, c.seed)
     x = S.bf16_normal((c.T, c.H), c.seed)
     w1 = S.bf16_normal((c.E, 2 * c.F, c.H), c.seed + 1, std=0.02)
     w2 = S.bf16_normal((c.E, c.H, c.F), c.seed + 2, std=0.02)
-    log("layer cfg1")
+    log("small layer")
     d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)
     y = d.layer(dev(x), dev(idx), dev(pr), dev(w1), dev(w2))
     torch.cuda.synchronize()
     assert int(d.flag.item()) == 0
     rt = oracle.route(idx, 0, c.E, c.K, pr, c.pad, -1, d.R)
     want = oracle.layer_tokens(np.arange(c.T), x, rt, lambda e, rows: oracle.expert_mlp_bf16(rows, w1[e], w2[e]))
-    _check_rows(host_bf16(y), want, "cfg1")
+    _check_rows(host_bf16(y), want, "small layer")
 
 
 @pytest.fixture(scope="module")
@@ -143,7 +143,7 @@ def dsv3_layer():
     """The DeepSeek-V3-shaped layer on one GPU: 8192 x 7168 bf16 tokens, 256
     experts top-8 (sigmoid, renormalised), FFN 2048, padding 128; weights drawn
     on the device (22.5 GB)."""
-    c = S.CONFIGS["cfg4_dsv3_layer"]
+    c = S.CONFIGS["dsv3_layer_8192x7168_e256"]
     idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
     x = S.bf16_normal((c.T, c.H), c.seed)
     w1 = S.weights_bf16(c.E, 2 * c.F, c.H, c.seed + 1, device=DEV)
@@ -162,7 +162,7 @@ def dsv3_layer():
 
 def test_dsv3_layer_sampled_expert_rows(dsv3_layer):
     L = dsv3_layer
-    log("layer cfg4 sampled rows")
+    log("layer shape, sampled rows")
     rt, c = L["rt"], L["c"]
     assert int(L["d"].flag.item()) == 0
     assert np.array_equal(L["d"].row_id.cpu().numpy(), rt["row_id"])
@@ -183,7 +183,7 @@ def test_dsv3_layer_sampled_expert_rows(dsv3_layer):
 
 def test_dsv3_layer_sampled_tokens(dsv3_layer):
     L = dsv3_layer
-    log("layer cfg4 sampled tokens")
+    log("layer shape, sampled tokens")
     toks = [0, 4095, 8191]
     w1, w2 = L["w1"], L["w2"]
     want = oracle.layer_tokens(toks, L["x"], L["rt"],
@@ -194,7 +194,7 @@ def test_dsv3_layer_sampled_tokens(dsv3_layer):
 def test_dsv3_combine_from_gpu_expert_out(dsv3_layer):
     """Combine over the real expert outputs for a token sample."""
     L = dsv3_layer
-    log("layer cfg4 combine")
+    log("layer shape, combine")
     toks = np.arange(0, 8192, 37)
     rt = L["rt"]
     rid = rt["row_id"][toks]
@@ -209,7 +209,7 @@ def test_layer_graph_replay_matches_eager():
     """The bf16 layer captured once in a HIP graph and replayed with new
     inputs (copied into the captured buffers) equals the eager result bit for
     bit, replay after replay."""
-    c = S.CONFIGS["cfg1_small_layer"]
+    c = S.CONFIGS["small_layer_512x1024"]
     w1 = dev(S.bf16_normal((c.E, 2 * c.F, c.H), 301, std=0.02)).view(torch.bfloat16)
     w2 = dev(S.bf16_normal((c.E, c.H, c.F), 302, std=0.02)).view(torch.bfloat16)
     d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)

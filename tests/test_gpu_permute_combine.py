@@ -48,12 +48,12 @@ def test_permute_and_combine_identity_full_size():
     """8192 x 7168 bf16, 32 experts, top-8 uniform routing, softmax probs,
     capacity 1.5x the largest count: byte-exact permute; identity experts and
     probabilities summing to 1 give back x exactly."""
-    c = S.CONFIGS["cfg2_permute_combine"]
+    c = S.CONFIGS["permute_combine_8192x7168_e32"]
     idx, pr = S.route_uniform_distinct(c.T, c.E, c.K, c.seed)
     base = oracle.route(idx, 0, c.E, c.K, pr)
     cap = oracle.capacity_from_rows(int(base["counts"].max()), 1.5)
     x = S.bf16_normal((c.T, c.H), c.seed)
-    log("permute+combine cfg2", cap)
+    log("permute+combine, 32-expert shape", cap)
     d = Dispatcher(c.T, c.H, c.E, c.K, capacity=cap)
     xd = dev(x)
     out_probs = torch.empty(d.R, dtype=torch.float32, device=DEV)
@@ -75,7 +75,7 @@ def test_permute_and_combine_identity_full_size():
 
 def test_combine_weighted_matches_oracle():
     """Random expert outputs (not identity), probabilities, dropped copies."""
-    c = S.CONFIGS["cfg2_permute_combine"]
+    c = S.CONFIGS["permute_combine_8192x7168_e32"]
     T = 2048
     idx, pr = S.route_uniform_distinct(T, c.E, c.K, 5)
     base = oracle.route(idx, 0, c.E, c.K, pr)
@@ -118,11 +118,11 @@ def test_combine_top1_is_exact_inverse():
 def test_permute_fp8_stress_full_size(fmt):
     """8192 x 7168 e4m3 payload with per-128-column scales, 256 experts,
     top-36 Zipf routing; dense and sparse encodings give byte-identical output."""
-    c = S.CONFIGS["cfg3_route_stress_fp8"]
+    c = S.CONFIGS["route_stress_fp8_8192x7168_e256"]
     idx, pr = S.route_zipf_gumbel(c.T, c.E, c.K, c.seed)
     routing = idx if fmt == oracle.FMT_DENSE_I16 else S.dense_to_sparse(idx, c.E)[0]
     xq, xs = S.quantize_rows_fp8_torch(S.bf16_normal((c.T, c.H), c.seed))
-    log("permute fp8 cfg3", fmt)
+    log("permute fp8, routing stress", fmt)
     d = Dispatcher(c.T, c.H, c.E, c.K, route_fmt="dense_i16" if fmt == 0 else "sparse_bool", payload="fp8")
     out, _, flag, _, osc = d.dispatch(dev(xq), dev(routing), x_scales=dev(xs))
     torch.cuda.synchronize()

@@ -50,16 +50,16 @@ def test_random_routing_matches_oracle(seed):
 
 def _workload(name):
     c = S.CONFIGS[name]
-    if name == "cfg1_small_layer":
+    if name == "small_layer_512x1024":
         return c, S.route_softmax_topk(c.T, c.E, c.K, c.seed)
-    if name == "cfg2_permute_combine":
+    if name == "permute_combine_8192x7168_e32":
         return c, S.route_uniform_distinct(c.T, c.E, c.K, c.seed)
-    if name == "cfg3_route_stress_fp8":
+    if name == "route_stress_fp8_8192x7168_e256":
         return c, S.route_zipf_gumbel(c.T, c.E, c.K, c.seed)
     return c, S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
 
 
-@pytest.mark.parametrize("name", ["cfg1_small_layer", "cfg2_permute_combine", "cfg4_dsv3_layer"])
+@pytest.mark.parametrize("name", ["small_layer_512x1024", "permute_combine_8192x7168_e32", "dsv3_layer_8192x7168_e256"])
 def test_workload_routing_matches_oracle(name):
     c, (idx, pr) = _workload(name)
     log("route workload", name)
@@ -73,7 +73,7 @@ def test_workload_routing_matches_oracle(name):
 def test_stress_routing_dense_and_sparse(with_probs):
     """8192 tokens, 256 experts, top-36, Zipf-skewed: both encodings match the
     oracle and each other."""
-    c, (idx, pr) = _workload("cfg3_route_stress_fp8")
+    c, (idx, pr) = _workload("route_stress_fp8_8192x7168_e256")
     m, pe = S.dense_to_sparse(idx, c.E, pr)
     log("route stress", with_probs)
     gd, _ = gpu_route(idx, oracle.FMT_DENSE_I16, c.E, c.K, pr if with_probs else None)
@@ -88,7 +88,7 @@ def test_stress_routing_dense_and_sparse(with_probs):
 
 
 def test_capacity_factors_and_overflow():
-    c, (idx, pr) = _workload("cfg2_permute_combine")
+    c, (idx, pr) = _workload("permute_combine_8192x7168_e32")
     base = oracle.route(idx, 0, c.E, c.K, pr)
     mx = int(base["counts"].max())
     for cap in [mx, oracle.capacity_from_rows(mx, 1.5), oracle.capacity_from_rows(mx, 2.0), mx - 1, mx // 2]:
@@ -101,7 +101,7 @@ def test_capacity_factors_and_overflow():
 
 @pytest.mark.parametrize("T", [0, 1, 16, 63, 64, 65, 100, 256])
 def test_decode_sizes_with_live_trim(T):
-    c = S.CONFIGS["cfg5_decode_fp8"]
+    c = S.CONFIGS["decode_fp8_7168_e256"]
     bucket = S.next_pow2_bucket(T)
     idx, pr = S.route_sigmoid_topk(bucket, c.E, c.K, c.seed + T)
     log("route decode", T, bucket)
@@ -122,7 +122,7 @@ def test_large_token_count_and_max_experts():
 
 
 def test_repeated_preprocess_is_deterministic():
-    c, (idx, pr) = _workload("cfg4_dsv3_layer")
+    c, (idx, pr) = _workload("dsv3_layer_8192x7168_e256")
     g1, d = gpu_route(idx, 0, c.E, c.K, pr, c.pad)
     import torch
     from gpu_util import dev

@@ -171,7 +171,7 @@ def test_expert_mlp_fp8_matches_numpy():
 def test_layer_tokens_composes_route_mlp_combine():
     """Sampled-token layer output equals the full permute -> per-expert MLP
     -> combine pipeline on a small problem."""
-    c = S.CONFIGS["cfg1_small_layer"]
+    c = S.CONFIGS["small_layer_512x1024"]
     T, E, K, H, F = 64, 4, 2, 128, 64
     idx, pr = S.route_softmax_topk(T, E, K, 61)
     rt = oracle.route(idx, 0, E, K, pr, pad=c.pad)

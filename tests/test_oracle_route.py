@@ -155,12 +155,12 @@ def _invariants(rt, T, K, pad, cap):
     assert bool(rt["flag"] & oracle.FLAG_CAPACITY) == (cap >= 0 and rt["counts"].max(initial=0) > cap)
 
 
-@pytest.mark.parametrize("name", ["cfg1_small_layer", "cfg2_permute_combine", "cfg4_dsv3_layer"])
+@pytest.mark.parametrize("name", ["small_layer_512x1024", "permute_combine_8192x7168_e32", "dsv3_layer_8192x7168_e256"])
 def test_invariants_on_workload_routing(name):
     c = S.CONFIGS[name]
-    if name == "cfg1_small_layer":
+    if name == "small_layer_512x1024":
         idx, pr = S.route_softmax_topk(c.T, c.E, c.K, c.seed)
-    elif name == "cfg2_permute_combine":
+    elif name == "permute_combine_8192x7168_e32":
         idx, pr = S.route_uniform_distinct(c.T, c.E, c.K, c.seed)
     else:
         idx, pr = S.route_sigmoid_topk(c.T, c.E, c.K, c.seed)
@@ -192,7 +192,7 @@ def test_capacity_checks_from_the_pages():
     """Capacity 1x, 1.5x, 2x the largest count: identical to the uncapped
     dispatch, flag clear; capacity at half: flag set, kept copies are each
     expert's earliest tokens.  One below the largest count also overflows."""
-    c = S.CONFIGS["cfg2_permute_combine"]
+    c = S.CONFIGS["permute_combine_8192x7168_e32"]
     T = 2048
     idx, pr = S.route_uniform_distinct(T, c.E, c.K, c.seed)
     base = oracle.route(idx, oracle.FMT_DENSE_I16, c.E, c.K, pr)
