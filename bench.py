@@ -190,6 +190,17 @@ def main() -> int:
     permute_combine = {"GB_s": round(pc_bytes / (pc_ms * 1e-3) / 1e9, 1),
                        "frac_of_peak": round(pc_bytes / (pc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        "permute_GB_s": stages["permute"]["GB_s"], "combine_GB_s": stages["combine"]["GB_s"]}
+    # practical HBM ceilings measured beside them (outside the timed region):
+    # a 1 GiB device copy (half reads, half writes) and a 1 GiB fill (writes
+    # only; the permute is 89 % writes, the combine 89 % reads)
+    ca = torch.empty(2 ** 29, dtype=torch.int16, device=dev)
+    cb = torch.empty_like(ca)
+    cmin, _ = _event_times(lambda: cb.copy_(ca))
+    fmin, _ = _event_times(lambda: cb.fill_(1))
+    permute_combine["copy_1GiB_GB_s"] = round(2 * 2 ** 30 / (cmin * 1e-3) / 1e9, 1)
+    permute_combine["fill_1GiB_GB_s"] = round(2 ** 30 / (fmin * 1e-3) / 1e9, 1)
+    permute_combine["permute_frac_of_fill"] = round(stages["permute"]["GB_s"] / permute_combine["fill_1GiB_GB_s"], 4)
+    del ca, cb
 
     # ---- HIP-graph replay of the whole step ------------------------------------
     graph = None
@@ -377,7 +388,8 @@ def run_decode(args):
 def run_extra(args):
     """The other synthetic workloads, timed on their own (not part of the
     step above): permute/combine with identity experts, the fp8 routing
-    stress, decode buckets with fp8 weights, and a plain device copy."""
+    stress, decode buckets with fp8 weights, and a plain device copy and
+    fill as practical HBM ceilings."""
     import numpy as np
     import torch
 
@@ -392,6 +404,9 @@ def run_extra(args):
     b = torch.empty_like(a)
     mn, md = _event_times(lambda: b.copy_(a))
     res["device_copy_1GiB"] = {"min_ms": round(mn, 4), "GB_s": round(2 * 2 ** 30 / (mn * 1e-3) / 1e9, 1)}
+    # practical write ceiling (the permute is 89 % writes): a 1 GiB fill
+    mn, md = _event_times(lambda: b.fill_(1))
+    res["device_fill_1GiB"] = {"min_ms": round(mn, 4), "GB_s": round(2 ** 30 / (mn * 1e-3) / 1e9, 1)}
     del a, b
 
     # permute + combine, 8192 x 7168 bf16, 32 experts top-8, capacity 1.5x
