@@ -152,9 +152,11 @@ __global__ __launch_bounds__(256) void k_combine_wg(const u32x4* __restrict__ Y,
 }
 
 // Combine from the fp8 format: expert-output rows are e4m3 codes with one
-// fp32 scale per 128 columns.  Same slicing and copy look-ahead as k_combine;
-// a 16-byte chunk holds 16 codes of one 128-column block, dequantised as
-// code value * scale in fp32 before the probability-weighted fma.
+// fp32 scale per 128 columns.  Same work split (a workgroup per token for
+// large batches, column slices otherwise) and copy look-ahead as the bf16
+// combine; a 16-byte chunk holds 16 codes of one 128-column block,
+// dequantised as code value * scale in fp32 before the probability-weighted
+// fma.
 constexpr int kCombQU = 2;   // 16-byte chunks (16 codes) per lane per pass
 
 __global__ __launch_bounds__(256) void k_combine_fp8(const u32x4* __restrict__ Yq, const float* __restrict__ Ys,
@@ -162,16 +164,23 @@ __global__ __launch_bounds__(256) void k_combine_fp8(const u32x4* __restrict__ Y
                                                      const int32_t* __restrict__ row_id,
                                                      const float* __restrict__ copy_prob, int apply,
                                                      u32x4* __restrict__ y) {
-    const int lane = threadIdx.x & 63;
-    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int t = wv / nsplit;
+    // nsplit == 0: one workgroup per token, the row's 64-chunk pieces dealt
+    // to its four wavefronts in turn (as k_combine_wg); else one wavefront per
+    // (token, slice of slice_ch chunks)
+    const int lane = threadIdx.x & 63, w4 = threadIdx.x >> 6;
+    const bool wg = nsplit == 0;
+    const int wv = blockIdx.x * 4 + w4;
+    const int t = wg ? (int)blockIdx.x : wv / nsplit;
     if (t >= T) return;
-    const int cs = (wv - t * nsplit) * slice_ch;
-    const int ce = min(nch, cs + slice_ch);
+    const int cs = wg ? 0 : (wv - t * nsplit) * slice_ch;
+    const int ce = wg ? nch : min(nch, cs + slice_ch);
+    const int step = wg ? 4 * 64 * kCombQU : 64 * kCombQU;
+    // chunk of slot u in the pass starting at c0
+    auto col = [&](int c0, int u) { return wg ? c0 + (u * 4 + w4) * 64 + lane : c0 + u * 64 + lane; };
     const int nsb = nch / 8;   // scales per row
     const int32_t* rid = row_id + (size_t)t * K;
     const float* cp = copy_prob + (size_t)t * K;
-    for (int c0 = cs; c0 < ce; c0 += 64 * kCombQU) {
+    for (int c0 = cs; c0 < ce; c0 += step) {
         float acc[kCombQU][16];
 #pragma unroll
         for (int u = 0; u < kCombQU; ++u)
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(256) void k_combine_fp8(const u32x4* __restrict__ Y
                 const size_t rr = (size_t)(ok[jj] ? r : 0);
 #pragma unroll
                 for (int u = 0; u < kCombQU; ++u) {
-                    const int c = c0 + u * 64 + lane;
+                    const int c = col(c0, u);
                     const bool in = ok[jj] && c < ce;
                     v[jj][u] = in ? __builtin_nontemporal_load(Yq + rr * nch + c) : u32x4{0u, 0u, 0u, 0u};
                     sc[jj][u] = in ? Ys[rr * nsb + (c >> 3)] : 0.f;
@@ -216,7 +225,7 @@ __global__ __launch_bounds__(256) void k_combine_fp8(const u32x4* __restrict__ Y
         }
 #pragma unroll
         for (int u = 0; u < kCombQU; ++u) {
-            const int c = c0 + u * 64 + lane;
+            const int c = col(c0, u);
             if (c < ce) {
                 u32x4 o0, o1;
 #pragma unroll
@@ -240,7 +249,11 @@ hipError_t launch_combine_fp8(const moe_handle* h, const void* yq, const float* 
     const int nch = d.H / 16;
     int nsplit, slice_ch;
     row_slices(d.T, nch, &nsplit, &slice_ch);
-    const long long waves = (long long)d.T * nsplit;
+    long long waves = (long long)d.T * nsplit;
+    if (d.T >= kWgMinTokens) {   // one workgroup per token
+        nsplit = 0;
+        waves = 4LL * d.T;
+    }
     hipLaunchKernelGGL(k_combine_fp8, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, (const u32x4*)yq, ys, d.T,
                        d.K, nch, (int)d.out_rows, nsplit, slice_ch, h->row_id, h->copy_prob, apply_probs,
                        (u32x4*)y_out);
