@@ -182,6 +182,67 @@ def test_permute_fp8_small_batch(T, H, E, K):
     assert int(flag.item()) == 0
 
 
+@pytest.mark.parametrize("T,H", [(4096, 1000), (4097, 2056), (5000, 520)])
+def test_workgroup_per_token_ragged_rows(T, H):
+    """At 4096 tokens and more, permute and combine take one workgroup per
+    token with 1 KB pieces dealt to its wavefronts in turn.  Row widths whose
+    last piece is partial (H/8 chunks not a multiple of 64), with capacity
+    drops: permuted rows byte-exact, weighted combine against the oracle,
+    dispatch + identity combine round-trips the kept tokens."""
+    E, K, cap = 9, 3, None
+    r = np.random.default_rng(T + H)
+    idx = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int16)
+    lg = r.standard_normal((T, K))
+    pr = (np.exp(lg) / np.exp(lg).sum(axis=1, keepdims=True)).astype(np.float32)
+    cap = int(T * K / E * 0.98)                     # a few copies dropped
+    x = S.bf16_normal((T, H), T + 5)
+    log("workgroup per token, ragged", T, H, cap)
+    d = Dispatcher(T, H, E, K, pad_multiple=2, capacity=cap)
+    perm, *_ = d.dispatch(dev(x), dev(idx), dev(pr))
+    Y = S.bf16_normal((d.R, H), T + 6)
+    y = d.combine(dev(Y))
+    yi = d.combine(perm)
+    torch.cuda.synchronize()
+    rt = oracle.route(idx, 0, E, K, pr, 2, cap, d.R)
+    rows = _kept_rows(rt["src_row"])
+    assert np.array_equal(host_bf16(perm)[rows], oracle.permute_rows(x, rt["row_id"], d.R)[rows])
+    want = oracle.combine_bf16(Y, rt["row_id"], rt["copy_prob"])
+    g, w = S.bf16_to_float(host_bf16(y)), S.bf16_to_float(want)
+    assert row_rel_l2(g, w).max() < 1e-2
+    assert np.mean(host_bf16(y) == want) > 0.99
+    full = (rt["row_id"] >= 0).all(axis=1)          # tokens with every copy kept
+    assert np.array_equal(host_bf16(yi)[full], x[full])
+
+
+@pytest.mark.parametrize("T,H", [(4096, 1152), (4100, 1920)])
+def test_workgroup_per_token_fp8_ragged_rows(T, H):
+    """fp8 rows (H/16 chunks, not a multiple of 64) through the workgroup-per-
+    token permute (codes and scales byte-exact) and the fp8 combine format's
+    workgroup-per-token combine (against the oracle on the same codes)."""
+    E, K = 6, 2
+    r = np.random.default_rng(T * 3 + H)
+    idx = np.argsort(r.random((T, E)), axis=1)[:, :K].astype(np.int16)
+    pr = np.full((T, K), 0.5, np.float32)
+    xq, xs = S.quantize_rows_fp8_torch(S.bf16_normal((T, H), T + 8))
+    log("workgroup per token, fp8 ragged", T, H)
+    d = Dispatcher(T, H, E, K, payload="fp8", pad_multiple=4)
+    out, _, flag, _, osc = d.dispatch(dev(xq), dev(idx), dev(pr), x_scales=dev(xs))
+    torch.cuda.synchronize()
+    rt = oracle.route(idx, 0, E, K, pr, 4, -1, d.R)
+    rows = _kept_rows(rt["src_row"])
+    assert np.array_equal(out.cpu().numpy()[rows], oracle.permute_rows(xq, rt["row_id"], d.R)[rows])
+    wsc = oracle.permute_rows(xs, rt["row_id"], d.R)
+    assert np.array_equal(osc.cpu().numpy()[rows].view(np.uint32), wsc[rows].view(np.uint32))
+    assert int(flag.item()) == 0
+    # the permuted codes and scales are a valid fp8 combine input
+    yc = d.combine_fp8(out, osc)
+    torch.cuda.synchronize()
+    want = oracle.combine_fp8(out.cpu().numpy(), osc.cpu().numpy(), rt["row_id"], rt["copy_prob"])
+    g = host_bf16(yc)
+    assert row_rel_l2(S.bf16_to_float(g), S.bf16_to_float(want)).max() < 1e-2
+    assert np.mean(g == want) > 0.99
+
+
 def test_empty_batch():
     log("empty batch")
     d = Dispatcher(0, 256, 8, 2, pad_multiple=16)
