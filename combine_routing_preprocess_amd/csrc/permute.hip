@@ -9,14 +9,15 @@
 // Token-major: each token's row is read once into registers (16-byte loads)
 // and stored to each of the token's k destinations, so HBM sees the
 // algorithmic minimum, T row reads + (kept copies) row writes.
-//  * Large batches (k_permute_wg): one workgroup of four wavefronts per
-//    token.  The row is cut into 1 KB pieces dealt to the wavefronts in
-//    turn, so the four wavefronts store adjacent pieces at the same time and
-//    each destination row receives 4 KB bursts.  Measured on MI355X this
-//    beats one wavefront per token, which writes its own 1 KB pieces one
-//    after another (0.205 against 0.214 ms at 8192 x 7168, top-8).
-//  * Small batches (k_permute): a token's row is cut into `nsplit` column
-//    slices so that enough wavefronts run; one wavefront per (token, slice).
+// The row is cut into 1 KB pieces (64 16-byte chunks), one wavefront per
+// (token, piece): a wavefront loads one 16-byte chunk per lane and stores it
+// to each kept destination, then exits.  Consecutive wavefronts hold
+// adjacent pieces of a token, so each destination row is written in bursts
+// of adjacent 1 KB pieces.  Measured on MI355X, many short wavefronts write
+// faster than few long ones: 0.190 ms at 8192 x 7168, top-8, against 0.200
+// ms for one workgroup per token and 0.214 ms for one wavefront per token
+// (a 1 GiB fill likewise reaches 6.9 TB/s with one 1 KB store per
+// wavefront and 5.6 with sixteen).
 // Row writes bypass cache residency (non-temporal stores): the permuted
 // buffer is far larger than the last-level cache and is consumed by another
 // kernel.  Row reads are ordinary loads: measured on MI355X, non-temporal
@@ -27,7 +28,8 @@
 namespace moe {
 namespace {
 
-constexpr int kPermU = 7;   // 16-byte chunks held per lane per pass
+constexpr int kPermU = 1;   // 16-byte chunks held per lane per pass
+constexpr int kPermSlice = 64;   // chunks per wavefront (one 1 KB piece)
 
 __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, int T, int K, int nch, int R,
                                                  int nsplit, int slice_ch, const int32_t* __restrict__ row_id,
@@ -61,48 +63,6 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
         }
     }
     if (xs && sl == 0) {
-        for (int j = 0; j < K; ++j) {
-            const int r = rid[j];
-            if (r < 0 || r >= R) continue;
-            for (int i = lane; i < nsc; i += 64) outs[(size_t)r * nsc + i] = xs[(size_t)t * nsc + i];
-        }
-    }
-}
-
-// Large batches: one workgroup per token; wavefront w holds the row's 1 KB
-// pieces w, w+4, w+8, ... (64 16-byte chunks each) and stores them to every
-// kept destination of the token.
-constexpr int kWgPieces = 4;       // pieces per wavefront per pass
-constexpr int kWgMinTokens = 4096; // below this, the sliced kernel keeps more wavefronts busy
-
-__global__ __launch_bounds__(256) void k_permute_wg(const u32x4* __restrict__ x, int T, int K, int nch, int R,
-                                                    const int32_t* __restrict__ row_id, u32x4* __restrict__ out,
-                                                    const float* __restrict__ xs, float* __restrict__ outs,
-                                                    int nsc) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t = blockIdx.x;
-    if (t >= T) return;
-    const u32x4* src = x + (size_t)t * nch;
-    const int32_t* rid = row_id + (size_t)t * K;
-    for (int p0 = 0; p0 * 256 < nch; p0 += kWgPieces) {
-        u32x4 v[kWgPieces];
-#pragma unroll
-        for (int u = 0; u < kWgPieces; ++u) {
-            const int c = ((p0 + u) * 4 + w) * 64 + lane;
-            if (c < nch) v[u] = src[c];
-        }
-        for (int j = 0; j < K; ++j) {
-            const int r = rid[j];
-            if (r < 0 || r >= R) continue;
-            u32x4* dst = out + (size_t)r * nch;
-#pragma unroll
-            for (int u = 0; u < kWgPieces; ++u) {
-                const int c = ((p0 + u) * 4 + w) * 64 + lane;
-                if (c < nch) __builtin_nontemporal_store(v[u], dst + c);
-            }
-        }
-    }
-    if (xs && w == 0) {
         for (int j = 0; j < K; ++j) {
             const int r = rid[j];
             if (r < 0 || r >= R) continue;
@@ -198,14 +158,8 @@ hipError_t launch_permute(const moe_handle* h, const void* x, const float* x_sca
     const int row_bytes = fp8 ? d.H : d.H * 2;
     const int nch = row_bytes / 16;
     const int nsc = fp8 ? d.H / 128 : 0;
-    if (d.T >= kWgMinTokens) {
-        hipLaunchKernelGGL(k_permute_wg, dim3((unsigned)d.T), dim3(256), 0, s, (const u32x4*)x, d.T, d.K, nch,
-                           (int)d.out_rows, h->row_id, (u32x4*)out, fp8 ? x_scales : nullptr,
-                           fp8 ? out_scales : nullptr, nsc);
-        return hipGetLastError();
-    }
-    int nsplit, slice_ch;
-    row_slices(d.T, nch, &nsplit, &slice_ch);
+    const int slice_ch = kPermSlice;
+    const int nsplit = (nch + slice_ch - 1) / slice_ch;
     const long long waves = (long long)d.T * nsplit;
     hipLaunchKernelGGL(k_permute, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, (const u32x4*)x, d.T, d.K, nch,
                        (int)d.out_rows, nsplit, slice_ch, h->row_id, (u32x4*)out, fp8 ? x_scales : nullptr,
