@@ -75,35 +75,32 @@ __global__ __launch_bounds__(256) void k_probs_gather(const int32_t* __restrict_
     }
 }
 
-// Combine backward: a token's row is cut into `nsl` column slices of up to
-// 64 * NPL chunks, one wavefront per slice, 4 / nsl tokens per workgroup.
-// Each wavefront holds its slice of grad_y in registers; per copy it issues
-// the expert-output loads, writes the row gradient, then reduces its partial
-// dot product (lane order, then a butterfly) into LDS.  After a workgroup
-// barrier the first wavefront of each token adds the slices' partials in
-// slice order.  Row ids and probabilities are loaded one copy ahead.
-template <int NPL>
-__global__ __launch_bounds__(256) void k_combine_backward(const u32x4* __restrict__ gy, const u32x4* __restrict__ Y,
-                                                          int T, int K, int E, int nch, int R, int nsl,
-                                                          const int32_t* __restrict__ row_id,
-                                                          const float* __restrict__ copy_prob, int apply,
-                                                          const int64_t* __restrict__ seg_off, int sparse,
-                                                          u32x4* __restrict__ gY, float* __restrict__ grad_probs) {
-    extern __shared__ float part[];   // [4][K] per-wavefront partial dot of each copy
+// Combine backward: a token's row is cut into 1 KB pieces (64 16-byte
+// chunks), one wavefront per piece, as many tokens per 16-wavefront
+// workgroup as fit whole (one token of up to 16 pieces, 8192 bf16).  Each
+// wavefront holds its chunk of grad_y in registers; per copy it issues the
+// expert-output load, writes the row gradient, then reduces its partial dot
+// product (butterfly) into LDS.  After a workgroup barrier the first
+// wavefront of each token adds the pieces' partials in piece order.  Row ids
+// and probabilities are loaded one copy ahead.  Measured on MI355X at 8192 x
+// 7168, top-8, many short wavefronts beat fewer long ones here as in the
+// permute: 0.404 ms against 0.415 ms with 4 KB slices of four wavefronts.
+__global__ __launch_bounds__(1024) void k_combine_backward(const u32x4* __restrict__ gy, const u32x4* __restrict__ Y,
+                                                           int T, int K, int E, int nch, int R, int nsl,
+                                                           const int32_t* __restrict__ row_id,
+                                                           const float* __restrict__ copy_prob, int apply,
+                                                           const int64_t* __restrict__ seg_off, int sparse,
+                                                           u32x4* __restrict__ gY, float* __restrict__ grad_probs) {
+    extern __shared__ float part[];   // [16][K] per-wavefront partial dot of each copy
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * (4 / nsl) + wave / nsl;
-    const int sl = wave % nsl;
-    const int cs = sl * 64 * NPL;
-    const bool active = t < T;
+    const int tpb = 16 / nsl;   // tokens per workgroup
+    const int t = blockIdx.x * tpb + wave / nsl;
+    const int c = (wave % nsl) * 64 + lane;
+    const bool active = t < T && wave < tpb * nsl;
+    const bool in_row = c < nch;
     const bool want_dot = grad_probs != nullptr && apply;
     if (active) {
-        u32x4 g[NPL];
-        const u32x4* src = gy + (size_t)t * nch;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const int c = cs + lane + 64 * i;
-            g[i] = c < nch ? src[c] : u32x4{0u, 0u, 0u, 0u};
-        }
+        const u32x4 g = in_row ? gy[(size_t)t * nch + c] : u32x4{0u, 0u, 0u, 0u};
         const int32_t* rid = row_id + (size_t)t * K;
         const float* cp = copy_prob + (size_t)t * K;
         int r_next = rid[0];
@@ -119,36 +116,22 @@ __global__ __launch_bounds__(256) void k_combine_backward(const u32x4* __restric
                 if (want_dot && lane == 0) part[wave * K + j] = 0.f;
                 continue;
             }
-            u32x4 y[NPL];
-            if (want_dot) {
-                const u32x4* yr = Y + (size_t)r * nch;
+            u32x4 y = {0u, 0u, 0u, 0u};
+            if (want_dot && in_row) y = __builtin_nontemporal_load(Y + (size_t)r * nch + c);
+            if (in_row) {
+                u32x4 o;
 #pragma unroll
-                for (int i = 0; i < NPL; ++i) {
-                    const int c = cs + lane + 64 * i;
-                    y[i] = c < nch ? __builtin_nontemporal_load(yr + c) : u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-            u32x4* dst = gY + (size_t)r * nch;
-#pragma unroll
-            for (int i = 0; i < NPL; ++i) {
-                const int c = cs + lane + 64 * i;
-                if (c < nch) {
-                    u32x4 o;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        o[q] = bf16_mul_rn(w, bf16_lo(g[i][q])) | (bf16_mul_rn(w, bf16_hi(g[i][q])) << 16);
-                    __builtin_nontemporal_store(o, dst + c);
-                }
+                for (int q = 0; q < 4; ++q)
+                    o[q] = bf16_mul_rn(w, bf16_lo(g[q])) | (bf16_mul_rn(w, bf16_hi(g[q])) << 16);
+                __builtin_nontemporal_store(o, gY + (size_t)r * nch + c);
             }
             if (want_dot) {
                 float dot = 0.f;
 #pragma unroll
-                for (int i = 0; i < NPL; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        dot = fmaf(bf16_lo(g[i][q]), bf16_lo(y[i][q]), dot);
-                        dot = fmaf(bf16_hi(g[i][q]), bf16_hi(y[i][q]), dot);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    dot = fmaf(bf16_lo(g[q]), bf16_lo(y[q]), dot);
+                    dot = fmaf(bf16_hi(g[q]), bf16_hi(y[q]), dot);
+                }
 #pragma unroll
                 for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, 64);
                 if (lane == 0) part[wave * K + j] = dot;
@@ -157,7 +140,7 @@ __global__ __launch_bounds__(256) void k_combine_backward(const u32x4* __restric
     }
     if (grad_probs == nullptr) return;   // uniform over the workgroup
     __syncthreads();
-    if (!active || sl != 0) return;
+    if (!active || wave % nsl != 0) return;
     for (int j = lane; j < K; j += 64) {
         const int r = row_id[(size_t)t * K + j];
         const bool kept = r >= 0 && r < R;
@@ -169,7 +152,7 @@ __global__ __launch_bounds__(256) void k_combine_backward(const u32x4* __restric
     }
 }
 
-// One wavefront per token for rows longer than 4 slices of 64*8 chunks: the
+// One wavefront per token for rows longer than 16 pieces of 64 chunks: the
 // gradient row is re-read from cache for every copy.
 __global__ __launch_bounds__(256) void k_combine_backward_long(const u32x4* __restrict__ gy,
                                                                const u32x4* __restrict__ Y, int T, int K, int E,
@@ -222,8 +205,7 @@ __global__ __launch_bounds__(256) void k_combine_backward_long(const u32x4* __re
     }
 }
 
-constexpr int kNpl = 4;       // chunks per lane of a slice held in registers
-constexpr int kMaxSlices = 4; // slices per row (rows up to 4 * 64 * 4 chunks = 8192 bf16)
+constexpr int kMaxPieces = 16;   // 1 KB pieces per row in one workgroup (rows up to 8192 bf16)
 
 hipError_t fill_zero(float* p, long long n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
@@ -258,11 +240,11 @@ hipError_t launch_combine_backward(const moe_handle* h, const void* grad_y, cons
         if (e != hipSuccess) return e;
     }
     const int nch = d.H * 2 / 16;
-    const int nsl = nch <= 64 * kNpl ? 1 : nch <= 2 * 64 * kNpl ? 2 : 4;
-    if (nch <= kMaxSlices * 64 * kNpl) {
-        const int tpb = 4 / nsl;
-        const size_t lds = grad_probs ? (size_t)4 * d.K * sizeof(float) : 0;
-        hipLaunchKernelGGL(k_combine_backward<kNpl>, dim3((unsigned)((d.T + tpb - 1) / tpb)), dim3(256), lds, s,
+    const int nsl = (nch + 63) / 64;
+    if (nsl <= kMaxPieces) {
+        const int tpb = kMaxPieces / nsl;
+        const size_t lds = grad_probs ? (size_t)kMaxPieces * d.K * sizeof(float) : 0;
+        hipLaunchKernelGGL(k_combine_backward, dim3((unsigned)((d.T + tpb - 1) / tpb)), dim3(64 * kMaxPieces), lds, s,
                            (const u32x4*)grad_y, (const u32x4*)expert_out, d.T, d.K, d.E, nch, (int)d.out_rows, nsl,
                            h->row_id, h->copy_prob, apply_probs, h->seg_off, sparse, (u32x4*)grad_expert_out,
                            grad_probs);
