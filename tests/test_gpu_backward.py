@@ -27,10 +27,14 @@ def _ulp_diff(a_bits, b_bits):
 
 
 def _dot_tol(gy_f, Y_f, H):
-    """fp32 bound for the GPU's dot product: each lane sums 8 * ceil(H/512)
-    products in order, then 6 butterfly levels; plus the oracle's rounding of
-    its double result to float."""
-    n = 8 * ((H // 8 + 63) // 64) + 6
+    """fp32 bound for the GPU's dot product, from the depth of its summation
+    tree.  Rows of up to 16 pieces of 64 chunks: each lane sums the 8
+    products of its chunk in order, 6 butterfly levels reduce a piece, and
+    the pieces are added in order.  Longer rows: each lane sums 8 products
+    per chunk it walks, then 6 butterfly levels.  Plus the oracle's rounding
+    of its double result to float."""
+    pieces = (H // 8 + 63) // 64
+    n = (8 + 6 + pieces if pieces <= 16 else 8 * pieces + 6) + 1
     return n * 2.0 ** -24 * np.abs(gy_f * Y_f).sum(axis=-1)
 
 
@@ -52,6 +56,7 @@ CASES = [
     (129, 512, 8, 8, 1, 20, oracle.FMT_DENSE_I32),
     (257, 2056, 12, 3, 7, 40, oracle.FMT_SPARSE_U8),      # ragged row (257 chunks), drops
     (33, 8200, 6, 2, 1, -1, oracle.FMT_DENSE_I16),        # row longer than the register-held path
+    (40, 1536, 160, 96, 2, -1, oracle.FMT_DENSE_I32),     # K > 64: two passes of the probability sum
     (1, 8, 1, 1, 1, -1, oracle.FMT_DENSE_I16),
     (0, 256, 4, 2, 1, -1, oracle.FMT_DENSE_I16),
 ]
