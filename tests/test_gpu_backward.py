@@ -57,6 +57,8 @@ CASES = [
     (257, 2056, 12, 3, 7, 40, oracle.FMT_SPARSE_U8),      # ragged row (257 chunks), drops
     (33, 8200, 6, 2, 1, -1, oracle.FMT_DENSE_I16),        # row longer than the register-held path
     (40, 1536, 160, 96, 2, -1, oracle.FMT_DENSE_I32),     # K > 64: two passes of the probability sum
+    (20, 8192, 4, 2, 1, -1, oracle.FMT_DENSE_I16),        # 16 pieces: the longest row one workgroup holds
+    (5, 512, 1024, 1024, 1, -1, oracle.FMT_DENSE_I16),    # K = E = 1024, the largest partial table
     (1, 8, 1, 1, 1, -1, oracle.FMT_DENSE_I16),
     (0, 256, 4, 2, 1, -1, oracle.FMT_DENSE_I16),
 ]
