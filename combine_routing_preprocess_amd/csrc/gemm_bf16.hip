@@ -195,10 +195,14 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
     u32x4 sw0[NWL], sw1[NWL];
     auto gload = [&](u32x4 (&sw)[NWL], int kt) {
         // stages past the end re-read the last one (valid memory, L2 hits);
-        // keeps the number of loads in flight the same on every path
+        // keeps the number of loads in flight the same on every path.
+        // Weights are read once per layer: non-temporal loads, so they do not
+        // displace the token slices the XCD's units re-read from L2 (measured
+        // on MI355X: FC2 about 1 % faster, FC1 unchanged).
         const int k = min(kt, nk - 1) * (BK * 2);
 #pragma unroll
-        for (int b = 0; b < NWL; ++b) sw[b] = *(const gu32x4*)(wbase + ((size_t)wrow[b] * pitch + k) + voff);
+        for (int b = 0; b < NWL; ++b)
+            sw[b] = __builtin_nontemporal_load((const gu32x4*)(wbase + ((size_t)wrow[b] * pitch + k) + voff));
     };
     auto swrite = [&](const u32x4 (&sw)[NWL], int slot) {
         u32x4* wl = wlds + slot * W_SLOT + wsl;
@@ -451,6 +455,10 @@ static_assert(2 * X_CH == 2 * X_SLOT && NWSET * W_CH == 2 * W_SLOT, "128-row rin
 __device__ __forceinline__ void dma16v(const void* gptr, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds) : "memory", "m0");
 }
+// The same with the non-temporal cache policy, for data read once (weights).
+__device__ __forceinline__ void dma16v_nt(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(gptr), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 typedef __bf16 bf16x8h __attribute__((ext_vector_type(8)));
@@ -480,7 +488,7 @@ __device__ __forceinline__ void mainloop(u32x4* xring, u32x4* wring, const uint1
         if (q < nblk) dma16v(xbase + xofs[q] + kt * BK, xl0 + ((kt & 1) * X_CH + q * 256) * 16);
     };
     auto dma_w = [&](int kt, int q) {
-        dma16v(wbase + wofs[q] + kt * BK, wl0 + ((kt % NWSET) * W_CH + q * 256) * 16);
+        dma16v_nt(wbase + wofs[q] + kt * BK, wl0 + ((kt % NWSET) * W_CH + q * 256) * 16);
     };
     int woff[KS][4], xoff[KS][TBW];
 #pragma unroll
