@@ -29,10 +29,12 @@ FMT_SPARSE_U8 = 2
 
 
 def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain C11 + OpenMP)."""
+    """Compile the oracle with gcc (plain C11 + OpenMP).  The helpers are
+    exported symbols; -fno-semantic-interposition lets gcc inline them into
+    the loops that call them (same arithmetic, about 3x faster)."""
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-fno-semantic-interposition", "-shared", "-std=c11",
                                "-Wall", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _SO)
     return _SO

@@ -440,38 +440,41 @@ static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* y32 (nullable [n,H]): the FC2 sums rounded once to float, the value an    */
 /* fp8 output format quantises (below, combine in the fp8 format).            */
+/* Every output value is one sequential sum in ascending index order; the     */
+/* threads only split the independent (row, feature) and (row, output) pairs. */
 void orc_expert_mlp_bf16(int32_t n, int32_t H, int32_t F, const uint16_t* x,
                          const uint16_t* w1, const uint16_t* w2, uint16_t* y,
                          uint16_t* a_out /* nullable [n,F] */, float* y32) {
-#pragma omp parallel
-    {
-        uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
-#pragma omp for schedule(dynamic)
-        for (int32_t r = 0; r < n; r++) {
-            const uint16_t* xr = x + (int64_t)r * H;
-            for (int32_t i = 0; i < F; i++) {
-                const uint16_t* wg = w1 + (int64_t)i * H;
-                const uint16_t* wu = w1 + (int64_t)(F + i) * H;
-                double g = 0.0, u = 0.0;
-                for (int32_t h = 0; h < H; h++) {
-                    double xv = orc_bf16_to_double(xr[h]);
-                    g += xv * orc_bf16_to_double(wg[h]);
-                    u += xv * orc_bf16_to_double(wu[h]);
-                }
-                a[i] = orc_bf16_from_double(orc_silu(g) * u);
-            }
-            if (a_out) memcpy(a_out + (int64_t)r * F, a, sizeof(uint16_t) * (size_t)F);
-            for (int32_t o = 0; o < H; o++) {
-                const uint16_t* w = w2 + (int64_t)o * F;
-                double acc = 0.0;
-                for (int32_t i = 0; i < F; i++)
-                    acc += orc_bf16_to_double(a[i]) * orc_bf16_to_double(w[i]);
-                y[(int64_t)r * H + o] = orc_bf16_from_double(acc);
-                if (y32) y32[(int64_t)r * H + o] = (float)acc;
-            }
+    uint16_t* a = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)n * (size_t)F);
+    /* FC1 + SwiGLU: a[r,i] = bf16(silu(g) * u) */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t ri = 0; ri < (int64_t)n * F; ri++) {
+        const int32_t r = (int32_t)(ri / F), i = (int32_t)(ri % F);
+        const uint16_t* xr = x + (int64_t)r * H;
+        const uint16_t* wg = w1 + (int64_t)i * H;
+        const uint16_t* wu = w1 + (int64_t)(F + i) * H;
+        double g = 0.0, u = 0.0;
+        for (int32_t h = 0; h < H; h++) {
+            double xv = orc_bf16_to_double(xr[h]);
+            g += xv * orc_bf16_to_double(wg[h]);
+            u += xv * orc_bf16_to_double(wu[h]);
         }
-        free(a);
+        a[ri] = orc_bf16_from_double(orc_silu(g) * u);
     }
+    if (a_out) memcpy(a_out, a, sizeof(uint16_t) * (size_t)n * (size_t)F);
+    /* FC2: y[r,o] = bf16(sum_i a[r,i] * W2[o,i]) */
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t ro = 0; ro < (int64_t)n * H; ro++) {
+        const int32_t r = (int32_t)(ro / H), o = (int32_t)(ro % H);
+        const uint16_t* ar = a + (int64_t)r * F;
+        const uint16_t* w = w2 + (int64_t)o * F;
+        double acc = 0.0;
+        for (int32_t i = 0; i < F; i++)
+            acc += orc_bf16_to_double(ar[i]) * orc_bf16_to_double(w[i]);
+        y[ro] = orc_bf16_from_double(acc);
+        if (y32) y32[ro] = (float)acc;
+    }
+    free(a);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -514,43 +517,61 @@ void orc_expert_mlp_fp8(int32_t n, int32_t H, int32_t F, const uint16_t* x,
                         const uint8_t* w1q, const float* w1s, const uint8_t* w2q,
                         const float* w2s, uint16_t* y) {
     int32_t hb = H / 128, fb = F / 128;
+    /* the value of every e4m3 code, from the definition above (read back per weight) */
+    double code_val[256];
+    for (int c = 0; c < 256; c++) code_val[c] = orc_e4m3_to_double((uint8_t)c);
+    double* xd = (double*)malloc(sizeof(double) * (size_t)n * (size_t)H);   /* dequantised input rows */
+    float* af = (float*)malloc(sizeof(float) * (size_t)n * (size_t)F);     /* silu(g) * u, in float  */
+    double* ad = (double*)malloc(sizeof(double) * (size_t)n * (size_t)F);  /* dequantised a          */
+    /* quantise each input row per 1x128 block, keep its dequantised values */
 #pragma omp parallel
     {
         float* xf = (float*)malloc(sizeof(float) * (size_t)H);
         uint8_t* xq = (uint8_t*)malloc((size_t)H);
         float* xs = (float*)malloc(sizeof(float) * (size_t)hb);
-        double* xd = (double*)malloc(sizeof(double) * (size_t)H);
-        float* af = (float*)malloc(sizeof(float) * (size_t)F);
-        uint8_t* aq = (uint8_t*)malloc((size_t)F);
-        float* as = (float*)malloc(sizeof(float) * (size_t)fb);
-        double* ad = (double*)malloc(sizeof(double) * (size_t)F);
-#pragma omp for schedule(dynamic)
+#pragma omp for schedule(static)
         for (int32_t r = 0; r < n; r++) {
             for (int32_t h = 0; h < H; h++) xf[h] = (float)orc_bf16_to_double(x[(int64_t)r * H + h]);
             orc_quant_rows_e4m3_f32(1, H, xf, xq, xs);
-            for (int32_t h = 0; h < H; h++) xd[h] = orc_e4m3_to_double(xq[h]) * (double)xs[h / 128];
-            for (int32_t i = 0; i < F; i++) {
-                double g = 0.0, u = 0.0;
-                for (int32_t h = 0; h < H; h++) {
-                    double wg = orc_e4m3_to_double(w1q[(int64_t)i * H + h]) *
-                                (double)w1s[(int64_t)(i / 128) * hb + h / 128];
-                    double wu = orc_e4m3_to_double(w1q[(int64_t)(F + i) * H + h]) *
-                                (double)w1s[(int64_t)((F + i) / 128) * hb + h / 128];
-                    g += xd[h] * wg;
-                    u += xd[h] * wu;
-                }
-                af[i] = (float)(orc_silu(g) * u);
-            }
-            orc_quant_rows_e4m3_f32(1, F, af, aq, as);
-            for (int32_t i = 0; i < F; i++) ad[i] = orc_e4m3_to_double(aq[i]) * (double)as[i / 128];
-            for (int32_t o = 0; o < H; o++) {
-                double acc = 0.0;
-                for (int32_t i = 0; i < F; i++)
-                    acc += ad[i] * orc_e4m3_to_double(w2q[(int64_t)o * F + i]) *
-                           (double)w2s[(int64_t)(o / 128) * fb + i / 128];
-                y[(int64_t)r * H + o] = orc_bf16_from_double(acc);
-            }
+            for (int32_t h = 0; h < H; h++) xd[(int64_t)r * H + h] = orc_e4m3_to_double(xq[h]) * (double)xs[h / 128];
         }
-        free(xf); free(xq); free(xs); free(xd); free(af); free(aq); free(as); free(ad);
+        free(xf); free(xq); free(xs);
     }
+    /* FC1 + SwiGLU over every (row, feature) pair; each sum in ascending h */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t ri = 0; ri < (int64_t)n * F; ri++) {
+        const int32_t r = (int32_t)(ri / F), i = (int32_t)(ri % F);
+        const double* xr = xd + (int64_t)r * H;
+        double g = 0.0, u = 0.0;
+        for (int32_t h = 0; h < H; h++) {
+            double wg = code_val[w1q[(int64_t)i * H + h]] * (double)w1s[(int64_t)(i / 128) * hb + h / 128];
+            double wu = code_val[w1q[(int64_t)(F + i) * H + h]] * (double)w1s[(int64_t)((F + i) / 128) * hb + h / 128];
+            g += xr[h] * wg;
+            u += xr[h] * wu;
+        }
+        af[ri] = (float)(orc_silu(g) * u);
+    }
+    /* re-quantise a per 1x128 block */
+#pragma omp parallel
+    {
+        uint8_t* aq = (uint8_t*)malloc((size_t)F);
+        float* as = (float*)malloc(sizeof(float) * (size_t)fb);
+#pragma omp for schedule(static)
+        for (int32_t r = 0; r < n; r++) {
+            orc_quant_rows_e4m3_f32(1, F, af + (int64_t)r * F, aq, as);
+            for (int32_t i = 0; i < F; i++) ad[(int64_t)r * F + i] = orc_e4m3_to_double(aq[i]) * (double)as[i / 128];
+        }
+        free(aq); free(as);
+    }
+    /* FC2 over every (row, output) pair; each sum in ascending i */
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t ro = 0; ro < (int64_t)n * H; ro++) {
+        const int32_t r = (int32_t)(ro / H), o = (int32_t)(ro % H);
+        const double* ar = ad + (int64_t)r * F;
+        double acc = 0.0;
+        for (int32_t i = 0; i < F; i++)
+            acc += ar[i] * code_val[w2q[(int64_t)o * F + i]] * (double)w2s[(int64_t)(o / 128) * fb + i / 128];
+        y[ro] = orc_bf16_from_double(acc);
+    }
+    free(xd); free(af); free(ad);
 }
