@@ -235,6 +235,48 @@ class Dispatcher:
             _need(perm.dtype == torch.bfloat16 and tuple(perm.shape) == (self.R, self.H), "perm must be bf16 [R,H]")
             _need(perm_scales is None, "bf16 permuted rows take no scales")
 
+    def _check_w1(self, w1: torch.Tensor, w1_scales: Optional[torch.Tensor]):
+        """FC1 weights [E, 2F, H] (bf16, or e4m3 codes with [E, 2F/128, H/128]
+        float32 block scales) on this device; returns (F, wdtype)."""
+        self._dev(w1, "w1")
+        _need(w1.dim() == 3 and w1.shape[0] == self.E and w1.shape[2] == self.H and w1.shape[1] % 2 == 0
+              and w1.shape[1] > 0, f"w1 must be [E, 2F, H] = [{self.E}, 2F, {self.H}], got {tuple(w1.shape)}")
+        F = int(w1.shape[1]) // 2
+        return F, self._check_wdtype(w1, w1_scales, "w1", (self.E, 2 * F // 128, self.H // 128))
+
+    def _check_w2(self, w2: torch.Tensor, w2_scales: Optional[torch.Tensor]):
+        """FC2 weights [E, H, F] (bf16, or e4m3 codes with [E, H/128, F/128]
+        float32 block scales) on this device; returns (F, wdtype)."""
+        self._dev(w2, "w2")
+        _need(w2.dim() == 3 and w2.shape[0] == self.E and w2.shape[1] == self.H and w2.shape[2] > 0,
+              f"w2 must be [E, H, F] = [{self.E}, {self.H}, F], got {tuple(w2.shape)}")
+        F = int(w2.shape[2])
+        return F, self._check_wdtype(w2, w2_scales, "w2", (self.E, self.H // 128, F // 128))
+
+    def _check_wdtype(self, w, scales, name, scale_shape):
+        if w.dtype in _FP8_DTYPES:
+            _need(self.H % 128 == 0 and w.shape[1] % 128 == 0 and w.shape[2] % 128 == 0,
+                  f"fp8 {name} needs dimensions that are multiples of 128")
+            _need(scales is not None, f"fp8 {name} needs its 128x128 block scales")
+            self._dev(scales, f"{name}_scales")
+            _need(scales.dtype == torch.float32 and tuple(scales.shape) == scale_shape,
+                  f"{name}_scales must be float32 {scale_shape}, got {scales.dtype} {tuple(scales.shape)}")
+            return "fp8"
+        _need(w.dtype == torch.bfloat16, f"{name} must be bfloat16 or e4m3 codes, got {w.dtype}")
+        _need(scales is None, f"bf16 {name} takes no block scales")
+        return "bf16"
+
+    def _check_scratch(self, scratch: torch.Tensor, F: int, wdtype: str):
+        self._dev(scratch, "scratch")
+        need = self.mlp_scratch_bytes(F, wdtype)
+        _need(need > 0, f"invalid FFN width {F} for {wdtype} weights")
+        _need(scratch.numel() * scratch.element_size() >= need, f"scratch holds fewer than the {need} bytes needed")
+
+    def _check_expert_out(self, out: torch.Tensor):
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.R, self.H),
+              f"out must be bf16 [R, H] = [{self.R}, {self.H}]")
+
     def grouped_mlp(self, perm: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, *,
                     w1_scales: Optional[torch.Tensor] = None, w2_scales: Optional[torch.Tensor] = None,
                     scratch: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -243,26 +285,16 @@ class Dispatcher:
         (bf16, or e4m3 codes with 128x128 block scales).  With a handle of fp8
         payload, perm is e4m3 codes quantised on dispatch plus perm_scales
         (fp8 weights only)."""
-        fp8w = w1.dtype in _FP8_DTYPES
-        wdtype = "fp8" if fp8w else "bf16"
-        E, F2, H = w1.shape
-        F = F2 // 2
-        _need(E == self.E and H == self.H and tuple(w2.shape) == (self.E, self.H, F), "weight shapes")
-        for t, n in ((w1, "w1"), (w2, "w2")):
-            self._dev(t, n)
+        F, wdtype = self._check_w1(w1, w1_scales)
+        F2, wdtype2 = self._check_w2(w2, w2_scales)
+        _need(F2 == F and wdtype2 == wdtype, "w1 and w2 must share the FFN width and dtype")
         self._check_perm(perm, perm_scales)
-        if fp8w:
-            _need(w1_scales is not None and w2_scales is not None, "fp8 weights need block scales")
-            _need(tuple(w1_scales.shape) == (E, F2 // 128, H // 128) and tuple(w2_scales.shape) == (E, H // 128, F // 128),
-                  "block-scale shapes")
-        else:
-            _need(w1.dtype == torch.bfloat16 and w2.dtype == torch.bfloat16, "bf16 weights expected")
         if scratch is None:
             scratch = self.alloc_mlp_scratch(F, wdtype)
+        self._check_scratch(scratch, F, wdtype)
         if out is None:
             out = torch.empty((self.R, self.H), dtype=torch.bfloat16, device=self.device)
-        self._dev(out, "out")
-        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.R, self.H), "out must be bf16 [R,H]")
+        self._check_expert_out(out)
         A.check(A.lib().moe_grouped_swiglu_mlp(C.byref(self.h), F, _DT[wdtype], _ptr(perm), _ptr(perm_scales), _ptr(w1),
                                                _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(scratch),
                                                scratch.numel(), _ptr(out), _stream()), "moe_grouped_swiglu_mlp")
@@ -271,19 +303,30 @@ class Dispatcher:
     def fc1(self, perm: torch.Tensor, w1: torch.Tensor, scratch: torch.Tensor, w1_scales=None,
             perm_scales=None) -> None:
         """FC1 + SwiGLU of every kept row into ``scratch`` (the first half of
-        grouped_mlp)."""
-        F = w1.shape[1] // 2
-        wdtype = "fp8" if w1.dtype in _FP8_DTYPES else "bf16"
+        grouped_mlp).  The FFN width and weight dtype are remembered: fc2 on
+        this scratch must use the same."""
+        F, wdtype = self._check_w1(w1, w1_scales)
         self._check_perm(perm, perm_scales)
+        self._check_scratch(scratch, F, wdtype)
         A.check(A.lib().moe_grouped_fc1_swiglu(C.byref(self.h), F, _DT[wdtype], _ptr(perm), _ptr(perm_scales), _ptr(w1),
                                                _ptr(w1_scales), _ptr(scratch), scratch.numel(), _stream()),
                 "moe_grouped_fc1_swiglu")
+        self._fc1_done = (F, wdtype, scratch.data_ptr())
+
+    def _check_after_fc1(self, F: int, wdtype: str, scratch: torch.Tensor):
+        prev = getattr(self, "_fc1_done", None)
+        _need(prev is not None, "fc2 needs an fc1 on this Dispatcher first")
+        _need(prev == (F, wdtype, scratch.data_ptr()),
+              f"fc2 with FFN width {F} ({wdtype}) on scratch {scratch.data_ptr():#x} does not match the last fc1 "
+              f"(width {prev[0]} ({prev[1]}) on scratch {prev[2]:#x})")
 
     def fc2(self, w2: torch.Tensor, scratch: torch.Tensor, out: torch.Tensor, w2_scales=None) -> torch.Tensor:
         """FC2 from ``scratch`` into the caller-owned ``out`` (the second half
         of grouped_mlp)."""
-        F = w2.shape[2]
-        wdtype = "fp8" if w2.dtype in _FP8_DTYPES else "bf16"
+        F, wdtype = self._check_w2(w2, w2_scales)
+        self._check_scratch(scratch, F, wdtype)
+        self._check_after_fc1(F, wdtype, scratch)
+        self._check_expert_out(out)
         A.check(A.lib().moe_grouped_fc2(C.byref(self.h), F, _DT[wdtype], _ptr(w2), _ptr(w2_scales), _ptr(scratch),
                                         scratch.numel(), _ptr(out), _stream()), "moe_grouped_fc2")
         return out
@@ -292,10 +335,10 @@ class Dispatcher:
                    out_scales: Optional[torch.Tensor] = None):
         """FC2 (bf16 weights) into the fp8 combine format: returns (codes
         [R,H] uint8, scales [R,H/128] float32)."""
-        self._dev(w2, "w2")
-        _need(w2.dtype == torch.bfloat16 and w2.dim() == 3 and tuple(w2.shape[:2]) == (self.E, self.H),
-              "w2 must be bf16 [E,H,F]")
-        F = w2.shape[2]
+        F, wdtype = self._check_w2(w2, None)
+        _need(wdtype == "bf16", "the fp8 combine format is written from bf16 weights")
+        self._check_scratch(scratch, F, wdtype)
+        self._check_after_fc1(F, wdtype, scratch)
         if out is None:
             out = torch.empty((self.R, self.H), dtype=torch.uint8, device=self.device)
         if out_scales is None:
@@ -397,12 +440,18 @@ class Dispatcher:
         return out, grad_probs
 
     def layer(self, x, routing, probs, w1, w2, *, perm=None, scratch=None, expert_out=None, out=None,
-              w1_scales=None, w2_scales=None, T_live=None, apply_probs=True):
-        """dispatch -> grouped MLP -> combine on the current stream."""
+              w1_scales=None, w2_scales=None, T_live=None, apply_probs=True, check_overflow=False):
+        """dispatch -> grouped MLP -> combine on the current stream.  With
+        ``check_overflow``, a device-side assert on the overflow flag is
+        enqueued after the combine (no host wait; capturable).  Buffers the
+        caller omits are allocated per call."""
         perm, _, flag, _, _ = self.dispatch(x, routing, probs, out=perm, T_live=T_live)
         y = self.grouped_mlp(perm, w1, w2, w1_scales=w1_scales, w2_scales=w2_scales, scratch=scratch,
                              out=expert_out)
-        return self.combine(y, apply_probs=apply_probs, out=out)
+        y = self.combine(y, apply_probs=apply_probs, out=out)
+        if check_overflow:
+            assert_no_overflow(flag)
+        return y
 
 
 class BufferRing:

@@ -85,6 +85,19 @@ int check_handle(const moe_handle* h, bool need_routing) {
     return MOE_OK;
 }
 
+// Argument checks of a permute (shared by moe_permute and moe_dispatch, which
+// runs them before it enqueues the routing preprocessing).
+int check_permute_args(const moe_desc& d, const void* d_x, const float* d_x_scales, const void* d_out,
+                       const float* d_out_scales) {
+    const bool fp8 = d.payload == MOE_FP8E4M3_B128;
+    if (d.T > 0 && (!d_x || !d_out)) return MOE_EINVAL;
+    if (fp8 && d.T > 0 && (!d_x_scales || !d_out_scales)) return MOE_EINVAL;
+    if (!fp8 && (d_x_scales || d_out_scales)) return MOE_EDTYPE;
+    if ((d_x && !al16(d_x)) || (d_out && !al16(d_out))) return MOE_EALIGN;
+    if ((d_x_scales && !al4(d_x_scales)) || (d_out_scales && !al4(d_out_scales))) return MOE_EALIGN;
+    return MOE_OK;
+}
+
 int num_cu() {
     static int cache[64] = {0};
     int dev = 0;
@@ -195,13 +208,8 @@ int moe_permute(const moe_handle* h, const void* d_x, const float* d_x_scales, v
                 float* d_out_scales, void* stream) {
     int rc = check_handle(h, true);
     if (rc) return rc;
-    const moe_desc& d = h->desc;
-    const bool fp8 = d.payload == MOE_FP8E4M3_B128;
-    if (d.T > 0 && (!d_x || !d_out)) return MOE_EINVAL;
-    if (fp8 && d.T > 0 && (!d_x_scales || !d_out_scales)) return MOE_EINVAL;
-    if (!fp8 && (d_x_scales || d_out_scales)) return MOE_EDTYPE;
-    if ((d_x && !al16(d_x)) || (d_out && !al16(d_out))) return MOE_EALIGN;
-    if ((d_x_scales && !al4(d_x_scales)) || (d_out_scales && !al4(d_out_scales))) return MOE_EALIGN;
+    rc = check_permute_args(h->desc, d_x, d_x_scales, d_out, d_out_scales);
+    if (rc) return rc;
     return hip_rc(launch_permute(h, d_x, d_x_scales, d_out, d_out_scales, (hipStream_t)stream));
 }
 
@@ -221,13 +229,10 @@ int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs, con
                  float* d_out_probs, int32_t* d_tokens_per_expert, int32_t* d_flag, void* stream) {
     int rc = check_handle(h, false);
     if (rc) return rc;
-    const moe_desc& d = h->desc;
-    const bool fp8 = d.payload == MOE_FP8E4M3_B128;
-    // argument checks of the permute half before anything is enqueued
-    if (d.T > 0 && (!d_x || !d_out)) return MOE_EINVAL;
-    if (fp8 && d.T > 0 && (!d_x_scales || !d_out_scales)) return MOE_EINVAL;
-    if (!fp8 && (d_x_scales || d_out_scales)) return MOE_EDTYPE;
-    if ((d_x && !al16(d_x)) || (d_out && !al16(d_out))) return MOE_EALIGN;
+    // every argument check of the permute half runs before anything is
+    // enqueued, so a rejected call leaves the handle and outputs untouched
+    rc = check_permute_args(h->desc, d_x, d_x_scales, d_out, d_out_scales);
+    if (rc) return rc;
     rc = moe_route_preprocess(h, d_routing, d_probs, d_T_live, d_tokens_per_expert, d_out_probs, d_flag, stream);
     if (rc) return rc;
     return moe_permute(h, d_x, d_x_scales, d_out, d_out_scales, stream);

@@ -219,3 +219,90 @@ def test_scratch_sizing():
     assert L.moe_mlp_scratch_bytes(C.byref(h), 256, A.FP8E4M3_B128) >= R * 256 + R * 2 * 4
     assert L.moe_mlp_scratch_bytes(C.byref(h), 100, A.FP8E4M3_B128) == 0
     assert L.moe_mlp_scratch_bytes(C.byref(h), 0, A.BF16) == 0
+
+
+def test_dispatch_rejects_misaligned_scales_before_routing():
+    """moe_dispatch runs every permute argument check before it enqueues the
+    routing preprocessing: a misaligned scale pointer returns MOE_EALIGN with
+    nothing enqueued and the handle still without routing metadata."""
+    L = A.lib()
+    d = _desc(H=256, payload="fp8")
+    rc, h, base, n, _buf = _host_handle(d)
+    assert rc == 0
+    x = C.c_void_p(base)
+    odd = C.c_void_p(base + 2)
+    for xs, os_ in ((x, odd), (odd, x)):
+        assert L.moe_dispatch(C.byref(h), x, None, None, x, xs, x, os_, None, x, x, None) == A.MOE_EALIGN
+        assert h.state == 0
+    # the same checks on a bf16 payload: scales are refused as a dtype error
+    d = _desc(H=256)
+    rc, h, base, n, _buf = _host_handle(d)
+    x = C.c_void_p(base)
+    assert L.moe_dispatch(C.byref(h), x, None, None, x, x, x, None, None, x, x, None) == A.MOE_EDTYPE
+    assert L.moe_dispatch(C.byref(h), x, None, None, C.c_void_p(base + 8), None, x, None, None, x, x,
+                          None) == A.MOE_EALIGN
+    assert h.state == 0
+
+
+def _cpu_dispatcher(**kw):
+    """A Dispatcher whose workspace is host memory: handle initialisation only
+    carves addresses, and every check below fails before any library call
+    that would touch a device."""
+    import torch
+    from combine_routing_preprocess_amd import Dispatcher
+    args = dict(T=64, H=256, E=4, K=2)
+    args.update(kw)
+    return Dispatcher(args.pop("T"), args.pop("H"), args.pop("E"), args.pop("K"), device="cpu", **args), torch
+
+
+def test_mlp_binding_rejects_bad_weights_scratch_and_out():
+    import pytest
+    d, torch = _cpu_dispatcher()
+    E, H, F, R = 4, 256, 128, d.R
+    bf = torch.bfloat16
+    perm = torch.zeros((R, H), dtype=bf)
+    w1 = torch.zeros((E, 2 * F, H), dtype=bf)
+    w2 = torch.zeros((E, H, F), dtype=bf)
+    scratch = torch.zeros(d.mlp_scratch_bytes(F), dtype=torch.uint8)
+    out = torch.zeros((R, H), dtype=bf)
+    bad_w1 = [torch.zeros((E + 1, 2 * F, H), dtype=bf), torch.zeros((E, 2 * F, H + 8), dtype=bf),
+              torch.zeros((E, 2 * F + 1, H), dtype=bf), torch.zeros((E, 2 * F, H), dtype=torch.float32),
+              torch.zeros((2 * F, H), dtype=bf)]
+    for w in bad_w1:
+        with pytest.raises(ValueError):
+            d.fc1(perm, w, scratch)
+        with pytest.raises(ValueError):
+            d.grouped_mlp(perm, w, w2, scratch=scratch, out=out)
+    bad_w2 = [torch.zeros((E, H, F), dtype=torch.float16), torch.zeros((E, H + 8, F), dtype=bf),
+              torch.zeros((E - 1, H, F), dtype=bf), torch.zeros((E, H, 2 * F), dtype=bf)]
+    for w in bad_w2:
+        with pytest.raises(ValueError):
+            d.grouped_mlp(perm, w1, w, scratch=scratch, out=out)
+    # fp8 weights without, or with wrongly shaped, block scales
+    w1q = torch.zeros((E, 2 * F, H), dtype=torch.uint8)
+    w2q = torch.zeros((E, H, F), dtype=torch.uint8)
+    s1 = torch.ones((E, 2 * F // 128, H // 128))
+    with pytest.raises(ValueError):
+        d.grouped_mlp(perm, w1q, w2q, w2_scales=torch.ones((E, H // 128, F // 128)))
+    with pytest.raises(ValueError):
+        d.grouped_mlp(perm, w1q, w2q, w1_scales=s1, w2_scales=torch.ones((E, H // 128, 2)))
+    with pytest.raises(ValueError):
+        d.fc1(perm, w1, scratch, w1_scales=s1)                       # bf16 weights take no scales
+    # scratch too small, out of the wrong shape or dtype
+    with pytest.raises(ValueError):
+        d.fc1(perm, w1, scratch[:-1])
+    for o in (torch.zeros((R - 1, H), dtype=bf), torch.zeros((R, H), dtype=torch.float16)):
+        with pytest.raises(ValueError):
+            d.grouped_mlp(perm, w1, w2, scratch=scratch, out=o)
+    # fc2 needs an fc1 first, with the same FFN width, dtype and scratch
+    with pytest.raises(ValueError):
+        d.fc2(w2, scratch, out)
+    d._fc1_done = (F, "bf16", scratch.data_ptr())
+    with pytest.raises(ValueError):
+        d.fc2(torch.zeros((E, H, 2 * F), dtype=bf), torch.zeros(d.mlp_scratch_bytes(2 * F), dtype=torch.uint8), out)
+    with pytest.raises(ValueError):
+        d.fc2(w2, torch.zeros(d.mlp_scratch_bytes(F), dtype=torch.uint8), out)   # another scratch
+    with pytest.raises(ValueError):
+        d.fc2(w2, scratch, torch.zeros((R, H + 8), dtype=bf))
+    with pytest.raises(ValueError):
+        d.fc2_fp8out(torch.zeros((E, H, F), dtype=torch.uint8), scratch)

@@ -11,7 +11,7 @@ import torch
 
 import moe_synth as S
 import oracle
-from combine_routing_preprocess_amd import Dispatcher
+from combine_routing_preprocess_amd import Dispatcher, assert_no_overflow
 from gpu_util import DEV, FMT_NAME, dev, host_bf16, log
 
 pytestmark = pytest.mark.gpu
@@ -184,6 +184,7 @@ def test_backward_graph_replay_matches_eager():
     def step():
         d.dispatch_backward(G, gop, out=gx, grad_probs=gp)
         d.combine_backward(gy, Y, True, out=gY, grad_probs=gq)
+        assert_no_overflow(d.flag)            # captured; the forward routing fits
 
     def fill(i):
         G.copy_(dev(S.bf16_normal((d.R, H), 100 + i)))
@@ -191,6 +192,8 @@ def test_backward_graph_replay_matches_eager():
         gop.copy_(torch.from_numpy(np.random.default_rng(300 + i).standard_normal(d.R).astype(np.float32)))
 
     log("backward graph replay")
+    torch.cuda.synchronize()
+    assert int(d.flag.item()) == 0                                   # before any step with the device assert
     fill(0)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

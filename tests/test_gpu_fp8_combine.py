@@ -11,7 +11,7 @@ import torch
 
 import moe_synth as S
 import oracle
-from combine_routing_preprocess_amd import Dispatcher
+from combine_routing_preprocess_amd import Dispatcher, assert_no_overflow
 from gpu_util import DEV, dev, host_bf16, log, rel_l2, row_rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -158,8 +158,12 @@ def test_fp8_formats_graph_replay_matches_eager():
         d.fc1(perm, W1, scr)
         d.fc2_fp8out(W2, scr, out=eq, out_scales=es)
         d.combine_fp8(eq, es, out=y)
+        assert_no_overflow(d.flag)            # captured; the routing above fits
+        assert_no_overflow(dq.flag)
 
     log("fp8 formats graph replay")
+    torch.cuda.synchronize()
+    assert int(d.flag.item()) == 0 and int(dq.flag.item()) == 0     # before any step with the device assert
     xt.copy_(dev(x))
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

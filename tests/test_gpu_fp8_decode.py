@@ -8,7 +8,7 @@ import torch
 import moe_synth as S
 import oracle
 from combine_routing_preprocess_amd import Dispatcher
-from gpu_util import DEV, dev, host_bf16, log, rel_l2, row_rel_l2
+from gpu_util import DEV, dev, host_bf16, log, rel_l2, require_clear_flag, row_rel_l2
 
 pytestmark = pytest.mark.gpu
 TOL8 = 5e-2
@@ -67,8 +67,11 @@ def _decode_case(c, T):
     return bucket, idx, pr, x
 
 
-@pytest.mark.parametrize("T", [16, 100, 256])
-def test_decode_layer_sampled_tokens(fp8_weights, T):
+@pytest.mark.parametrize("T", [16, 64, 100, 256])
+def test_decode_layer_all_live_tokens(fp8_weights, T):
+    """The fp8 decode layer in buckets 16, 64, 128 (100 live tokens) and 256:
+    every live token against the oracle, and the tokens past the live count
+    exactly zero."""
     c, w1q, w1s, w2q, w2s = fp8_weights
     bucket, idx, pr, x = _decode_case(c, T)
     log("fp8 decode layer", T, bucket)
@@ -78,7 +81,7 @@ def test_decode_layer_sampled_tokens(fp8_weights, T):
     torch.cuda.synchronize()
     rt = oracle.route(idx, 0, c.E, c.K, pr, c.pad, -1, d.R, T)
     assert np.array_equal(d.row_id.cpu().numpy(), rt["row_id"])
-    toks = sorted({0, T - 1, T // 2})
+    toks = list(range(T))
     want = oracle.layer_tokens(toks, x, rt, lambda e, rows: oracle.expert_mlp_fp8(
         rows, w1q[e].cpu().numpy(), w1s[e].cpu().numpy(), w2q[e].cpu().numpy(), w2s[e].cpu().numpy()))
     _check(host_bf16(y[toks]), want, f"T {T}")
@@ -95,10 +98,14 @@ def test_decode_graph_replay_matches_eager(fp8_weights):
     for bucket in (16, 64):
         log("fp8 decode graph", bucket)
         d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
-        xb = torch.zeros((bucket, c.H), dtype=torch.bfloat16, device=DEV)
-        rb = torch.zeros((bucket, c.K), dtype=torch.int16, device=DEV)
-        pb = torch.zeros((bucket, c.K), dtype=torch.float32, device=DEV)
+        # captured buffers, filled with a valid routing before the warm-up and
+        # the capture: the step ends with the device-side overflow assert
+        _, idx, pr, x = _decode_case(c, bucket)
+        xb = dev(x).view(torch.bfloat16)
+        rb = dev(idx)
+        pb = dev(pr)
         tl = torch.tensor([bucket], dtype=torch.int32, device=DEV)
+        require_clear_flag(d, rb, pb, tl)
         perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
         scratch = d.alloc_mlp_scratch(c.F, "fp8")
         eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
@@ -106,7 +113,7 @@ def test_decode_graph_replay_matches_eager(fp8_weights):
 
         def step():
             d.layer(xb, rb, pb, w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl, perm=perm, scratch=scratch,
-                    expert_out=eo, out=yb)
+                    expert_out=eo, out=yb, check_overflow=True)
 
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -123,6 +130,7 @@ def test_decode_graph_replay_matches_eager(fp8_weights):
             rb.copy_(dev(idx))
             pb.copy_(dev(pr))
             tl.fill_(T)
+            require_clear_flag(d, rb, pb, tl)      # the replay recomputes this same flag
             g.replay()
             torch.cuda.synchronize()
             replay = yb.clone()

@@ -9,7 +9,7 @@ import torch
 import moe_synth as S
 import oracle
 from combine_routing_preprocess_amd import Dispatcher
-from gpu_util import DEV, dev, host_bf16, log, rel_l2, row_rel_l2
+from gpu_util import DEV, dev, host_bf16, log, rel_l2, require_clear_flag, row_rel_l2
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -167,7 +167,16 @@ def test_dsv3_layer_sampled_expert_rows(dsv3_layer):
     assert int(L["d"].flag.item()) == 0
     assert np.array_equal(L["d"].row_id.cpu().numpy(), rt["row_id"])
     counts = rt["counts"]
-    experts = sorted({int(counts.argmax()), int(counts.argmin()), 0, c.E - 1, 77})
+    # segments of up to 256 rows take one 256-row pass, 257..320 rows the
+    # 192-row units, longer ones 320-row chunks of 128-row passes: two experts
+    # of every class present, plus the largest, the smallest, the first and
+    # the last
+    experts = {int(counts.argmax()), int(counts.argmin()), 0, c.E - 1, 77}
+    for lo, hi in ((1, 256), (257, 320), (321, 1 << 30)):
+        cls = np.nonzero((counts >= lo) & (counts <= hi))[0]
+        experts.update(int(e) for e in cls[:1].tolist() + cls[-1:].tolist())
+    experts = sorted(experts)
+    log("experts sampled", experts, "rows", counts[experts].tolist())
     got_all = L["expert_out"]
     rng = np.random.default_rng(3)
     for e in experts:
@@ -182,12 +191,22 @@ def test_dsv3_layer_sampled_expert_rows(dsv3_layer):
 
 
 def test_dsv3_layer_sampled_tokens(dsv3_layer):
+    """Whole layer (routing, permute, FC1 + SwiGLU, FC2, combine) against the
+    oracle on 258 tokens spread over the batch: every 32nd token plus the
+    last one, each through all of its experts (about 2,000 expert rows)."""
     L = dsv3_layer
-    log("layer shape, sampled tokens")
-    toks = [0, 4095, 8191]
+    toks = sorted(set(range(0, 8192, 32)) | {4095, 8191})
+    log("layer shape, sampled tokens", len(toks))
     w1, w2 = L["w1"], L["w2"]
-    want = oracle.layer_tokens(toks, L["x"], L["rt"],
-                               lambda e, rows: oracle.expert_mlp_bf16(rows, host_bf16(w1[e]), host_bf16(w2[e])))
+    done = [0]
+
+    def expert(e, rows):
+        done[0] += 1
+        if done[0] % 32 == 0:
+            log("oracle experts done", done[0])
+        return oracle.expert_mlp_bf16(rows, host_bf16(w1[e]), host_bf16(w2[e]))
+
+    want = oracle.layer_tokens(toks, L["x"], L["rt"], expert)
     _check_rows(host_bf16(L["y"][toks]), want, "tokens")
 
 
@@ -213,17 +232,21 @@ def test_layer_graph_replay_matches_eager():
     w1 = dev(S.bf16_normal((c.E, 2 * c.F, c.H), 301, std=0.02)).view(torch.bfloat16)
     w2 = dev(S.bf16_normal((c.E, c.H, c.F), 302, std=0.02)).view(torch.bfloat16)
     d = Dispatcher(c.T, c.H, c.E, c.K, pad_multiple=c.pad)
-    xb = torch.zeros((c.T, c.H), dtype=torch.bfloat16, device=DEV)
-    rb = torch.zeros((c.T, c.K), dtype=torch.int16, device=DEV)
-    pb = torch.zeros((c.T, c.K), dtype=torch.float32, device=DEV)
+    # captured buffers, filled with a valid routing before the warm-up and the
+    # capture: the step ends with the device-side overflow assert
+    idx, pr = S.route_softmax_topk(c.T, c.E, c.K, 399)
+    xb = dev(S.bf16_normal((c.T, c.H), 499)).view(torch.bfloat16)
+    rb = dev(idx)
+    pb = dev(pr)
     perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
     scratch = d.alloc_mlp_scratch(c.F)
     eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
     yb = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
 
     def step():
-        d.layer(xb, rb, pb, w1, w2, perm=perm, scratch=scratch, expert_out=eo, out=yb)
+        d.layer(xb, rb, pb, w1, w2, perm=perm, scratch=scratch, expert_out=eo, out=yb, check_overflow=True)
 
+    require_clear_flag(d, rb, pb)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -238,6 +261,7 @@ def test_layer_graph_replay_matches_eager():
         xb.copy_(dev(S.bf16_normal((c.T, c.H), 500 + rep)).view(torch.bfloat16))
         rb.copy_(dev(idx))
         pb.copy_(dev(pr))
+        require_clear_flag(d, rb, pb)          # the replay recomputes this same flag
         g.replay()
         torch.cuda.synchronize()
         replay = yb.clone()

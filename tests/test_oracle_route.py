@@ -272,6 +272,82 @@ def test_page_value_capacity_calibration():
     assert oracle.capacity_from_rows(8, 1.0) == 8
 
 
+def _routing_with_counts(counts, T, K):
+    """Dense routing [T,K] in which expert e appears counts[e] times, each at
+    most once per token (requires counts[e] <= T and sum(counts) <= T*K;
+    unused slots are -1).  The copies are laid out slot-major in expert
+    order: position j*T + t of the flat list is slot j of token t, and a run
+    of at most T equal experts never reaches the same token twice."""
+    flat = np.full(T * K, -1, np.int64)
+    ids = np.repeat(np.arange(len(counts)), counts)
+    flat[:len(ids)] = ids
+    idx = flat.reshape(K, T).T.astype(np.int16)
+    for t in range(T):
+        row = idx[t][idx[t] >= 0]
+        assert len(set(row.tolist())) == len(row)
+    return idx
+
+
+def test_out_rows_bound_reached_by_each_term():
+    """The bound is reached exactly, through each of its two terms, by
+    routings built for it; together with the safety checks below this pins
+    it from both sides (a bound that is too large, e.g. padding E*p rows or
+    a capacity not rounded up to the padding multiple, fails here)."""
+    cases = 0
+    for E in range(1, 7):
+        for K in range(1, E + 1):
+            for pad in range(1, 5):
+                for T in range(1, 13):
+                    # copies term T*K + E*(pad-1): every expert holds a count
+                    # of 1 mod pad, so each segment carries pad-1 padding rows
+                    N = T * K
+                    if N >= E and (N - E) % pad == 0:
+                        counts = np.ones(E, np.int64)
+                        extra, e = (N - E) // pad, 0
+                        while extra and e < E:        # top experts up by pad, keeping counts <= T
+                            take = min(extra, (T - 1) // pad)
+                            counts[e] += take * pad
+                            extra -= take
+                            e += 1
+                        if extra == 0:
+                            idx = _routing_with_counts(counts, T, K)
+                            rt = oracle.route(idx, 0, E, K, pad=pad, R=10 ** 6)
+                            bound = oracle.out_rows_bound(T, E, K, pad, -1)
+                            assert rt["rows_needed"] == bound == N + E * (pad - 1), (T, E, K, pad)
+                            cases += 1
+                    # capacity term E*roundup(C, pad): every expert over capacity
+                    for C in range(0, T + 1):
+                        if E * T > N:
+                            continue          # not every expert can receive T copies
+                        counts = np.full(E, T, np.int64)
+                        idx = _routing_with_counts(counts, T, K)
+                        rt = oracle.route(idx, 0, E, K, pad=pad, cap=C, R=10 ** 6)
+                        bound = oracle.out_rows_bound(T, E, K, pad, C)
+                        if E * (-(-C // pad) * pad) <= N + E * (pad - 1):
+                            assert rt["rows_needed"] == bound, (T, E, K, pad, C)
+                            cases += 1
+    assert cases > 300
+
+
+def test_out_rows_bound_safe_exhaustive_tiny():
+    """No dense routing of up to 3 tokens, 3 experts, top-2 (empty slots
+    included) needs more rows than the bound, for every padding multiple
+    1 and 3 and capacity none, 1 and 2."""
+    for T in range(0, 4):
+        for E in range(1, 4):
+            for K in range(1, min(E, 2) + 1):
+                rows = list(itertools.product(range(-1, E), repeat=K))
+                rows = [r for r in rows if len({e for e in r if e >= 0}) == sum(e >= 0 for e in r)]
+                for pad in (1, 3):
+                    for cap in (-1, 1, 2):
+                        bound = oracle.out_rows_bound(T, E, K, pad, cap)
+                        worst = 0
+                        for combo in itertools.product(rows, repeat=T):
+                            idx = np.array(combo, np.int16).reshape(T, K)
+                            worst = max(worst, oracle.route(idx, 0, E, K, pad=pad, cap=cap, R=10 ** 6)["rows_needed"])
+                        assert worst <= bound, (T, E, K, pad, cap, worst, bound)
+
+
 def test_out_rows_bound_is_tight_and_safe():
     r = np.random.default_rng(7)
     for _ in range(200):
