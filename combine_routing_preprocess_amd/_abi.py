@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_route.so")
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EALIGN = 0, -1, -2, -3, -4
 MOE_ESTALE, MOE_EHIP, MOE_EUNSUPPORTED, MOE_ENOSPC = -5, -6, -7, -8
 MOE_EBUSY, MOE_ESTATE = -9, -10
+NOALLOC_SCRATCH_BYTES = 128 << 20      # MOE_NOALLOC_SCRATCH_BYTES
 RING_MAX_SLOTS = 32
 
 ROUTE_DENSE_I16, ROUTE_DENSE_I32, ROUTE_SPARSE_BOOL = 0, 1, 2
@@ -56,6 +57,8 @@ SIGNATURES = [
     ("moe_mlp_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32, C.c_int32]),
     ("moe_grouped_swiglu_mlp", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, _P,
                                          _P, C.c_size_t, _P, _P]),
+    ("moe_grouped_swiglu_mlp_noalloc", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, _P, _P,
+                                                 _P, _P, _P]),
     ("moe_grouped_fc1_swiglu", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, _P, _P,
                                          C.c_size_t, _P]),
     ("moe_grouped_fc2", C.c_int, [C.POINTER(MoeHandle), C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P, _P]),

@@ -300,6 +300,23 @@ class Dispatcher:
                                                scratch.numel(), _ptr(out), _stream()), "moe_grouped_swiglu_mlp")
         return out
 
+    def grouped_mlp_noalloc(self, perm: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, *,
+                            w1_scales: Optional[torch.Tensor] = None, w2_scales: Optional[torch.Tensor] = None,
+                            out: torch.Tensor, perm_scales: Optional[torch.Tensor] = None):
+        """grouped_mlp without a scratch argument and without any allocation:
+        the activations live in the library's fixed device array
+        (A.NOALLOC_SCRATCH_BYTES per GPU, shared by every call on that GPU).
+        ``out`` is required."""
+        F, wdtype = self._check_w1(w1, w1_scales)
+        F2, wdtype2 = self._check_w2(w2, w2_scales)
+        _need(F2 == F and wdtype2 == wdtype, "w1 and w2 must share the FFN width and dtype")
+        self._check_perm(perm, perm_scales)
+        self._check_expert_out(out)
+        A.check(A.lib().moe_grouped_swiglu_mlp_noalloc(C.byref(self.h), F, _DT[wdtype], _ptr(perm), _ptr(perm_scales),
+                                                       _ptr(w1), _ptr(w1_scales), _ptr(w2), _ptr(w2_scales), _ptr(out),
+                                                       _stream()), "moe_grouped_swiglu_mlp_noalloc")
+        return out
+
     def fc1(self, perm: torch.Tensor, w1: torch.Tensor, scratch: torch.Tensor, w1_scales=None,
             perm_scales=None) -> None:
         """FC1 + SwiGLU of every kept row into ``scratch`` (the first half of

@@ -251,19 +251,16 @@ size_t moe_mlp_scratch_bytes(const moe_handle* h, int32_t F, int32_t wdtype) {
 
 namespace {
 
-// Checks shared by the MLP entry points; *ncu receives the CU count.
-int check_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* w, const float* w_scales,
-              const void* scratch, size_t scratch_bytes, int* ncu) {
+// Host-side checks of one weight tensor of the MLP (no device access).
+int check_mlp_weights(const moe_handle* h, int32_t F, int32_t wdtype, const void* w, const float* w_scales) {
     int rc = check_handle(h, true);
     if (rc) return rc;
     const moe_desc& d = h->desc;
     if (F <= 0) return MOE_ESHAPE;
     if (d.payload != MOE_BF16 && wdtype != MOE_FP8E4M3_B128) return MOE_EDTYPE;
-    if (!w || !scratch) return MOE_EINVAL;
-    if (!al16(w) || !al16(scratch)) return MOE_EALIGN;
-    const size_t need = moe_mlp_scratch_bytes(h, F, wdtype);
-    if (need == 0) return MOE_ESHAPE;
-    if (scratch_bytes < need) return MOE_ENOSPC;
+    if (!w) return MOE_EINVAL;
+    if (!al16(w)) return MOE_EALIGN;
+    if (moe_mlp_scratch_bytes(h, F, wdtype) == 0) return MOE_ESHAPE;
     if (wdtype == MOE_BF16) {
         if (w_scales) return MOE_EDTYPE;
         if (d.H % 256 || F % 128) return MOE_ESHAPE;
@@ -274,11 +271,53 @@ int check_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* w, con
     } else {
         return MOE_EDTYPE;
     }
+    return MOE_OK;
+}
+
+// Checks shared by the MLP entry points; *ncu receives the CU count.
+int check_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const void* w, const float* w_scales,
+              const void* scratch, size_t scratch_bytes, int* ncu) {
+    int rc = check_mlp_weights(h, F, wdtype, w, w_scales);
+    if (rc) return rc;
+    if (!scratch) return MOE_EINVAL;
+    if (!al16(scratch)) return MOE_EALIGN;
+    if (scratch_bytes < moe_mlp_scratch_bytes(h, F, wdtype)) return MOE_ENOSPC;
     *ncu = num_cu();
     return *ncu > 0 ? MOE_OK : MOE_EHIP;
 }
 
+// Host checks of the permuted rows FC1 reads.
+int check_perm(const moe_handle* h, const void* d_perm, const float* d_perm_scales) {
+    // fp8 permuted rows (quantised on dispatch) carry their scales; bf16 rows none
+    const bool fp8_rows = h->desc.payload == MOE_FP8E4M3_B128;
+    if (fp8_rows != (d_perm_scales != nullptr)) return fp8_rows ? MOE_EINVAL : MOE_EDTYPE;
+    if (!d_perm) return MOE_EINVAL;
+    if (!al16(d_perm) || (d_perm_scales && !al4(d_perm_scales))) return MOE_EALIGN;
+    return MOE_OK;
+}
+
 }  // namespace
+
+}  // extern "C"
+
+namespace moe {
+
+int check_mlp_host(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm, const float* d_perm_scales,
+                   const void* d_w1, const float* d_w1_scales, const void* d_w2, const float* d_w2_scales,
+                   const void* d_expert_out) {
+    int rc = check_mlp_weights(h, F, wdtype, d_w2, d_w2_scales);
+    if (rc) return rc;
+    rc = check_mlp_weights(h, F, wdtype, d_w1, d_w1_scales);
+    if (rc) return rc;
+    rc = check_perm(h, d_perm, d_perm_scales);
+    if (rc) return rc;
+    if (!d_expert_out) return MOE_EINVAL;
+    return al16(d_expert_out) ? MOE_OK : MOE_EALIGN;
+}
+
+}  // namespace moe
+
+extern "C" {
 
 int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
                            const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
@@ -286,11 +325,8 @@ int moe_grouped_fc1_swiglu(const moe_handle* h, int32_t F, int32_t wdtype, const
     int ncu = 0;
     int rc = check_mlp(h, F, wdtype, d_w1, d_w1_scales, d_scratch, scratch_bytes, &ncu);
     if (rc) return rc;
-    // fp8 permuted rows (quantised on dispatch) carry their scales; bf16 rows none
-    const bool fp8_rows = h->desc.payload == MOE_FP8E4M3_B128;
-    if (fp8_rows != (d_perm_scales != nullptr)) return fp8_rows ? MOE_EINVAL : MOE_EDTYPE;
-    if (!d_perm) return MOE_EINVAL;
-    if (!al16(d_perm) || (d_perm_scales && !al4(d_perm_scales))) return MOE_EALIGN;
+    rc = check_perm(h, d_perm, d_perm_scales);
+    if (rc) return rc;
     if (wdtype == MOE_FP8E4M3_B128)
         return hip_rc(launch_gemm_fp8(h, 0, F, d_perm, d_perm_scales, d_w1, d_w1_scales, d_scratch, nullptr,
                                       (hipStream_t)stream));
@@ -330,8 +366,9 @@ int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const
     int ncu = 0;
     int rc = check_mlp(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, &ncu);
     if (rc) return rc;
-    if (!d_expert_out) return MOE_EINVAL;
-    if (!al16(d_expert_out)) return MOE_EALIGN;
+    // every host check of both halves runs before FC1 is enqueued
+    rc = check_mlp_host(h, F, wdtype, d_perm, d_perm_scales, d_w1, d_w1_scales, d_w2, d_w2_scales, d_expert_out);
+    if (rc) return rc;
     rc = moe_grouped_fc1_swiglu(h, F, wdtype, d_perm, d_perm_scales, d_w1, d_w1_scales, d_scratch,
                                 scratch_bytes, stream);
     if (rc) return rc;

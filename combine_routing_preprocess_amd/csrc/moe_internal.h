@@ -41,6 +41,12 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     return (uint32_t)p;
 }
 
+// Every host-side argument check of moe_grouped_swiglu_mlp except those of
+// the scratch buffer (no device access); returns a moe_status.
+int check_mlp_host(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm, const float* d_perm_scales,
+                   const void* d_w1, const float* d_w1_scales, const void* d_w2, const float* d_w2_scales,
+                   const void* d_expert_out);
+
 // ---- launchers (each returns a hipError_t) --------------------------------
 hipError_t launch_route(const moe_handle* h, const void* routing, const float* probs,
                         const int32_t* T_live, int32_t* tokens_per_expert, float* out_probs,

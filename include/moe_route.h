@@ -255,6 +255,29 @@ int moe_grouped_fc2(const moe_handle* h, int32_t F, int32_t wdtype, const void* 
                     const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
                     void* d_expert_out, void* stream);
 
+/* Grouped expert MLP that allocates nothing, for callers that cannot call
+ * hipMalloc or take a caller-provided scratch buffer (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * operation, arguments and requirements as moe_grouped_swiglu_mlp, minus the
+ * scratch: the FC1 -> FC2 activations live in a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends (its address is looked up once per device, at the
+ * first call with that device current).
+ *   Returns MOE_ENOSPC, with nothing enqueued, when
+ *   moe_mlp_scratch_bytes(h, F, wdtype) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *   (128 MiB: the bf16 path up to R*F = 64 Mi activations, the fp8 path up to
+ *   about 7,500 rows at H = 7168, F = 2048, which holds the 5,888-row bound
+ *   of a 256-token decode bucket with 256 experts top-8 and padding 16).
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents (nothing in it needs to start at zero): calls that can
+ *   overlap on one GPU (different streams without ordering between them)
+ *   race on it and must be serialised by the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES (128ll << 20)
+int moe_grouped_swiglu_mlp_noalloc(const moe_handle* h, int32_t F, int32_t wdtype, const void* d_perm,
+                                   const float* d_perm_scales, const void* d_w1, const float* d_w1_scales,
+                                   const void* d_w2, const float* d_w2_scales, void* d_expert_out,
+                                   void* stream);
+
 /* FC2 into the fp8 combine format: as moe_grouped_fc2 (bf16 weights), but each
  * kept row's fp32 output is quantised per 1x128 block (scale = block amax /
  * 448, 1 for an all-zero block; code = e4m3(y / scale), nearest-even,

@@ -306,3 +306,26 @@ def test_mlp_binding_rejects_bad_weights_scratch_and_out():
         d.fc2(w2, scratch, torch.zeros((R, H + 8), dtype=bf))
     with pytest.raises(ValueError):
         d.fc2_fp8out(torch.zeros((E, H, F), dtype=torch.uint8), scratch)
+
+
+def test_noalloc_mlp_rejects_sizes_beyond_its_array_on_the_host():
+    """moe_grouped_swiglu_mlp_noalloc refuses a problem whose activations do
+    not fit its fixed device array before touching any device."""
+    L = A.lib()
+    d = _desc(T=8192, H=7168, E=256, K=8, pad_multiple=128)
+    rc, h, base, n, _buf = _host_handle(d)
+    assert rc == 0
+    assert L.moe_mlp_scratch_bytes(C.byref(h), 2048, A.BF16) > A.NOALLOC_SCRATCH_BYTES
+    x = C.c_void_p(base)
+    assert L.moe_grouped_swiglu_mlp_noalloc(C.byref(h), 2048, A.BF16, x, None, x, None, x, None, x,
+                                            None) == A.MOE_ESTALE      # no routing metadata yet
+    h.state = 1   # as if routing had been enqueued; every case below fails before any device call
+    assert L.moe_grouped_swiglu_mlp_noalloc(C.byref(h), 2048, A.BF16, x, None, x, None, x, None, x,
+                                            None) == A.MOE_ENOSPC
+    assert L.moe_grouped_swiglu_mlp_noalloc(C.byref(h), 100, A.BF16, x, None, x, None, x, None, x,
+                                            None) == A.MOE_ESHAPE
+    assert L.moe_grouped_swiglu_mlp_noalloc(None, 2048, A.BF16, x, None, x, None, x, None, x, None) == A.MOE_EINVAL
+    assert L.moe_grouped_swiglu_mlp_noalloc(C.byref(h), 2048, A.BF16, x, None, x, None, x, None, None,
+                                            None) == A.MOE_EINVAL
+    assert L.moe_grouped_swiglu_mlp_noalloc(C.byref(h), 2048, A.BF16, x, None, x, None, x, None,
+                                            C.c_void_p(base + 8), None) == A.MOE_EALIGN
