@@ -70,6 +70,9 @@ SIGNATURES = [
     ("moe_ring_acquire", C.c_int, [C.POINTER(MoeRing), _P, C.POINTER(C.c_void_p), C.POINTER(C.c_int32)]),
     ("moe_ring_release", C.c_int, [C.POINTER(MoeRing), C.c_int32, _P]),
     ("moe_ring_destroy", C.c_int, [C.POINTER(MoeRing)]),
+    ("moe_decode_layer_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32]),
+    ("moe_decode_layer_fp8", C.c_int, [C.POINTER(MoeHandle), C.c_int32, _P, _P, _P, _P, _P, _P, C.c_size_t, _P,
+                                       C.c_int32, _P, _P, _P]),
     ("moe_dispatch_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P, _P]),
     ("moe_combine_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, C.c_int32, _P, _P, _P]),
 ]

@@ -456,6 +456,37 @@ class Dispatcher:
                                              _ptr(out), _ptr(grad_probs), _stream()), "moe_combine_backward")
         return out, grad_probs
 
+    def decode_layer_scratch_bytes(self, F: int) -> int:
+        return int(A.lib().moe_decode_layer_scratch_bytes(C.byref(self.h), int(F)))
+
+    def decode_layer_fp8(self, x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, w1_scales: torch.Tensor,
+                         w2_scales: torch.Tensor, *, scratch: torch.Tensor, expert_out: torch.Tensor,
+                         out: torch.Tensor, status: torch.Tensor, apply_probs: bool = True) -> torch.Tensor:
+        """The rest of the layer after preprocess(), as one persistent kernel:
+        quantise-on-dispatch, FC1 + SwiGLU, activation quantiser, FC2 into
+        ``expert_out`` and the combine into ``out``, with fp8 weights.
+        ``status`` (one int32 on the device) is written 0, or 1 if a wait of
+        the kernel ran past its bound."""
+        _need(self.payload == A.BF16, "the decode layer takes bf16 token rows")
+        self._check_x(x)
+        F, wdtype = self._check_w1(w1, w1_scales)
+        F2, wdtype2 = self._check_w2(w2, w2_scales)
+        _need(wdtype == "fp8" and wdtype2 == "fp8" and F2 == F, "the decode layer takes fp8 w1 and w2 of one FFN width")
+        self._dev(scratch, "scratch")
+        need = self.decode_layer_scratch_bytes(F)
+        _need(need > 0 and scratch.numel() * scratch.element_size() >= need,
+              f"scratch holds fewer than the {need} bytes needed")
+        self._check_expert_out(expert_out)
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.T, self.H), "out must be bf16 [T,H]")
+        self._dev(status, "status")
+        _need(status.dtype == torch.int32 and status.numel() == 1, "status must be one int32")
+        A.check(A.lib().moe_decode_layer_fp8(C.byref(self.h), F, _ptr(x), _ptr(w1), _ptr(w1_scales), _ptr(w2),
+                                             _ptr(w2_scales), _ptr(scratch), scratch.numel(), _ptr(expert_out),
+                                             1 if apply_probs else 0, _ptr(out), _ptr(status), _stream()),
+                "moe_decode_layer_fp8")
+        return out
+
     def layer(self, x, routing, probs, w1, w2, *, perm=None, scratch=None, expert_out=None, out=None,
               w1_scales=None, w2_scales=None, T_live=None, apply_probs=True, check_overflow=False):
         """dispatch -> grouped MLP -> combine on the current stream.  With

@@ -19,13 +19,12 @@
 //    one wavefront per token at 8192 x 7168, top-8, on MI355X).
 //  * Small batches (k_combine): a token's row is cut into `nsplit` column
 //    slices so that enough wavefronts run; one wavefront per (token, slice).
-#include "moe_internal.h"
+#include "device_ops.h"
 
 namespace moe {
 namespace {
 
-constexpr int kCombU = 4;   // 16-byte chunks per lane per pass
-constexpr int kCombJ = 4;   // copies loaded ahead of their multiply-adds
+using namespace ops;
 
 __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ Y, int T, int K, int nch, int R,
                                                  int nsplit, int slice_ch, const int32_t* __restrict__ row_id,
@@ -97,58 +96,9 @@ __global__ __launch_bounds__(256) void k_combine_wg(const u32x4* __restrict__ Y,
                                                    const int32_t* __restrict__ row_id,
                                                    const float* __restrict__ copy_prob, int apply,
                                                    u32x4* __restrict__ y) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int t = blockIdx.x;
     if (t >= T) return;
-    const int32_t* rid = row_id + (size_t)t * K;
-    const float* cp = copy_prob + (size_t)t * K;
-    for (int p0 = 0; p0 * 256 < nch; p0 += kCombU) {
-        float acc[kCombU][8];
-#pragma unroll
-        for (int u = 0; u < kCombU; ++u)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
-        for (int j0 = 0; j0 < K; j0 += kCombJ) {
-            u32x4 v[kCombJ][kCombU];
-            float pj[kCombJ];
-            bool ok[kCombJ];
-#pragma unroll
-            for (int jj = 0; jj < kCombJ; ++jj) {
-                const int j = j0 + jj;
-                const int r = j < K ? rid[j] : -1;
-                ok[jj] = r >= 0 && r < R;
-                pj[jj] = ok[jj] ? (apply ? cp[j] : 1.f) : 0.f;
-                const u32x4* src = Y + (size_t)(ok[jj] ? r : 0) * nch;
-#pragma unroll
-                for (int u = 0; u < kCombU; ++u) {
-                    const int c = ((p0 + u) * 4 + w) * 64 + lane;
-                    v[jj][u] = (ok[jj] && c < nch) ? __builtin_nontemporal_load(src + c) : u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < kCombJ; ++jj) {
-                if (!ok[jj]) continue;
-#pragma unroll
-                for (int u = 0; u < kCombU; ++u)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[u][2 * q] = fmaf(pj[jj], bf16_lo(v[jj][u][q]), acc[u][2 * q]);
-                        acc[u][2 * q + 1] = fmaf(pj[jj], bf16_hi(v[jj][u][q]), acc[u][2 * q + 1]);
-                    }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kCombU; ++u) {
-            const int c = ((p0 + u) * 4 + w) * 64 + lane;
-            if (c < nch) {
-                u32x4 o;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    o[q] = f32_to_bf16(acc[u][2 * q]) | (f32_to_bf16(acc[u][2 * q + 1]) << 16);
-                y[(size_t)t * nch + c] = o;
-            }
-        }
-    }
+    combine_token_wg(Y, K, nch, R, row_id, copy_prob, apply, y, t, threadIdx.x >> 6, threadIdx.x & 63);
 }
 
 // Combine from the fp8 format: expert-output rows are e4m3 codes with one

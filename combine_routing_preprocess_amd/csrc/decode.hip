@@ -1,0 +1,242 @@
+// Persistent decode layer: quantise-on-dispatch -> FC1 + SwiGLU -> activation
+// quantiser -> FC2 -> combine in one launch, fed by device-side ticket queues
+// (fp8 e4m3 expert weights with 128x128 block scales; decode-sized batches).
+//
+// Operation: TensorRT-LLM PR #16190 "Update CuTeDSL MegaMoE kernels" (first
+// commit message: dispatch, FC1, FC2 and combine fused in one kernel for
+// decode, with loads that wait on flags written by the producing stage;
+// review-fix commit: the live-token trim and a launch that does nothing for
+// an empty batch) on top of the routing metadata of Megatron-LM PR #6800 /
+// DeepEP PR #716 (the same handle as the separate kernels).  The arithmetic
+// is that of the separate launches, unit for unit: quantise-on-dispatch,
+// the fp8 GEMM units, the row quantiser and the per-token combine are the
+// same device functions, so the layer output is bit-identical to theirs.
+//
+// Work items, in their global order (every dependency points to an earlier
+// item):
+//   D(t)     quantise token row t and write it to each kept copy's row
+//   F1(a,u)  FC1 + SwiGLU unit u of the a-th expert holding rows   needs all D
+//   Q(a)     quantise that expert's activation rows                 needs its F1
+//   F2(a,u)  FC2 unit u of the expert                               needs its Q
+//   C(t)     combine of token t                                     needs all F2
+// Items are spread over 8 queues (tokens t % 8, experts a % 8); each queue
+// lists its items in the global order and hands them out by an atomic ticket.
+// Workgroup b takes tickets from queue b % 8.  A workgroup only ever waits on
+// items of lower global order.  The lowest unfinished item is therefore
+// always claimable: everything its queue's workgroups hold is lower, hence
+// finished, so they take it next; its owner is running (a ticket is taken by
+// a running workgroup) and its own dependencies are finished.  Progress does
+// not depend on how many workgroups are resident at once.
+//
+// Completion is published with a release atomic add at agent scope after a
+// workgroup barrier (the producer's stores are written back from its XCD's
+// L2); a waiter polls the counter with agent-scope relaxed loads (coherent
+// across XCDs), then every thread takes an agent-scope acquire fence before
+// reading the produced data.  Every wait is bounded by the 100 MHz real-time
+// counter: past the bound it sets bit 0 of the caller's status word and
+// proceeds, and once the status is set later waits return at once, so the
+// kernel always runs to its end.
+#include "device_ops.h"
+
+namespace moe {
+namespace {
+
+using namespace ops;
+
+constexpr int kQueues = 8;
+constexpr int kCtlStride = 32;                        // ints between shared counters (128 bytes)
+constexpr int kCtlDispatch = kQueues * kCtlStride;    // D items done
+constexpr int kCtlFc2 = kCtlDispatch + kCtlStride;    // F2 items done (all experts)
+constexpr int kCtlFc1 = kCtlFc2 + kCtlStride;         // F1 items done, per active expert
+constexpr int kCtlQuant = kCtlFc1 + kMaxE;            // Q item done, per active expert
+constexpr int kCtlInts = kCtlQuant + kMaxE;
+constexpr long long kWaitTicks = 25000000;            // 0.25 s of the 100 MHz real-time counter
+
+struct DecodeArgs {
+    const uint16_t* x;          // [T,H] bf16 tokens
+    const int32_t* row_id;      // [T,K]
+    const float* copy_prob;     // [T,K]
+    const int64_t* seg_off;     // [E+1]
+    const int32_t* kept;        // [E]
+    const uint8_t* w1;          // [E,2F,H] e4m3
+    const float* w1s;           // [E,2F/128,H/128]
+    const uint8_t* w2;          // [E,H,F] e4m3
+    const float* w2s;           // [E,H/128,F/128]
+    uint8_t* xq;                // [R,H] token codes
+    float* xs;                  // [R,H/128]
+    float* act;                 // [R,F] fp32 SwiGLU output
+    uint8_t* aq;                // [R,F] activation codes
+    float* as;                  // [R,F/128]
+    uint16_t* eo;               // [R,H] bf16 expert output
+    uint16_t* y;                // [T,H] bf16 layer output
+    int* ctl;                   // kCtlInts control ints, zero at launch
+    int* status;                // bit 0: a wait ran past its bound
+    long long R;
+    int T, H, F, K, E, apply;
+};
+
+__global__ __launch_bounds__(256) void k_decode_reset(int* __restrict__ ctl, int n, int* __restrict__ status) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) ctl[i] = 0;
+    if (threadIdx.x == 0) status[0] = 0;
+}
+
+// Thread 0: wait until *c >= target (bounded); then every thread acquires.
+__device__ __forceinline__ void wait_count(const DecodeArgs& a, int* c, int target) {
+    if (threadIdx.x == 0) {
+        if (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+            const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+                    __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Publish one finished item: every thread's stores are done at the barrier,
+// then thread 0 releases them at agent scope with the counter increment.
+__device__ __forceinline__ void signal_done(int* c) {
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
+    __shared__ int s_list[kMaxE];    // experts holding rows, ascending
+    __shared__ int s_cnt;
+    __shared__ int s_ticket;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = blockIdx.x % kQueues;
+
+    // ---- experts holding rows (every workgroup builds the same list) ----------
+    if (wave == 0) {
+        int run = 0;
+        for (int c = 0; c < a.E; c += 64) {
+            const int e = c + lane;
+            bool has = false;
+            if (e < a.E) {
+                const long long so = a.seg_off[e];
+                long long mm = so < a.R ? (long long)a.kept[e] : 0;
+                if (so + mm > a.R) mm = a.R - so;
+                has = mm > 0;
+            }
+            const unsigned long long act = __ballot(has);
+            if (has) s_list[run + __popcll(act & ((1ull << lane) - 1ull))] = e;
+            run += __popcll(act);
+        }
+        if (lane == 0) s_cnt = run;
+    }
+    __syncthreads();
+    const int n_act = s_cnt;
+    const int upe1 = a.F / kFeat, upe2 = a.H / kFeat2;
+    // this queue's items: tokens q, q+8, ...; active experts q, q+8, ...
+    const int nD = a.T > q ? (a.T - q + kQueues - 1) / kQueues : 0;
+    const int nA = n_act > q ? (n_act - q + kQueues - 1) / kQueues : 0;
+    const int eF1 = nD + nA * upe1, eQ = eF1 + nA, eF2 = eQ + nA * upe2, eC = eF2 + nD;
+    const int nbH = a.H / 128, ngH = (nbH + kPQBlocks - 1) / kPQBlocks;
+    const int nbF = a.F / 128, ngF = (nbF + kQBlocks - 1) / kQBlocks;
+    int* ctl = a.ctl;
+
+    for (;;) {
+        if (tid == 0) s_ticket = __hip_atomic_fetch_add(ctl + q * kCtlStride, 1, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int i = s_ticket;
+        __syncthreads();                 // s_ticket is rewritten by the next claim
+        if (i >= eC) break;
+        if (i < nD) {
+            // D(t): quantise-on-dispatch of token t
+            const long long t = q + (long long)kQueues * i;
+            for (int g = wave; g < ngH; g += 4)
+                permute_quant_wave(a.x, a.H, a.K, (int)a.R, a.row_id, a.xq, a.xs, t, g * kPQBlocks, lane);
+            signal_done(ctl + kCtlDispatch);
+        } else if (i < eF1) {
+            const int k = i - nD, ai = q + kQueues * (k / upe1), u = k % upe1;
+            wait_count(a, ctl + kCtlDispatch, a.T);
+            fp8_unit<0>(a.xq, a.xs, a.w1, a.w1s, a.act, a.seg_off, a.kept, a.R, a.H, 2 * a.F, a.F, s_list[ai], u,
+                        lane, wave);
+            signal_done(ctl + kCtlFc1 + ai);
+        } else if (i < eQ) {
+            // Q(a): the expert's activation rows, (row, 8-block group) per wavefront
+            const int ai = q + kQueues * (i - eF1), e = s_list[ai];
+            wait_count(a, ctl + kCtlFc1 + ai, upe1);
+            const long long seg = a.seg_off[e];
+            long long me = a.kept[e];
+            if (seg + me > a.R) me = a.R - seg;
+            for (long long w = wave; w < me * ngF; w += 4)
+                quant_row_wave<float>(a.act, a.F, a.aq, a.as, seg + w / ngF, (int)(w % ngF) * kQBlocks, lane);
+            signal_done(ctl + kCtlQuant + ai);
+        } else if (i < eF2) {
+            const int k = i - eQ, ai = q + kQueues * (k / upe2), u = k % upe2;
+            wait_count(a, ctl + kCtlQuant + ai, 1);
+            fp8_unit<1>(a.aq, a.as, a.w2, a.w2s, a.eo, a.seg_off, a.kept, a.R, a.F, a.H, a.H, s_list[ai], u, lane,
+                        wave);
+            signal_done(ctl + kCtlFc2);
+        } else {
+            // C(t): combine of token t once every FC2 unit is done
+            const int t = q + kQueues * (i - eF2);
+            wait_count(a, ctl + kCtlFc2, n_act * upe2);
+            combine_token_wg((const u32x4*)a.eo, a.K, a.H / 8, (int)a.R, a.row_id, a.copy_prob, a.apply,
+                             (u32x4*)a.y, t, wave, lane);
+            __syncthreads();
+        }
+    }
+}
+
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t decode_layer_scratch_bytes(long long R, int H, int F) {
+    return up256(fp8_mlp_scratch_bytes(R, H, F)) + up256((size_t)kCtlInts * 4);
+}
+
+hipError_t launch_decode_layer(const moe_handle* h, int F, const void* x, const void* w1, const float* w1s,
+                               const void* w2, const float* w2s, void* scratch, void* expert_out, int apply_probs,
+                               void* y, int32_t* status, int num_cu, hipStream_t s) {
+    const moe_desc& d = h->desc;
+    const long long R = d.out_rows;
+    // the scratch regions of the fp8 expert MLP, then the control ints
+    char* base = (char*)scratch;
+    DecodeArgs a;
+    a.act = (float*)base;
+    a.xq = (uint8_t*)(base + up256((size_t)R * F * 4));
+    a.xs = (float*)((char*)a.xq + up256((size_t)R * d.H));
+    a.aq = (uint8_t*)((char*)a.xs + up256((size_t)R * (d.H / 128) * 4));
+    a.as = (float*)((char*)a.aq + up256((size_t)R * F));
+    a.ctl = (int*)(base + up256(fp8_mlp_scratch_bytes(R, d.H, F)));
+    a.x = (const uint16_t*)x;
+    a.row_id = h->row_id;
+    a.copy_prob = h->copy_prob;
+    a.seg_off = h->seg_off;
+    a.kept = h->kept;
+    a.w1 = (const uint8_t*)w1;
+    a.w1s = w1s;
+    a.w2 = (const uint8_t*)w2;
+    a.w2s = w2s;
+    a.eo = (uint16_t*)expert_out;
+    a.y = (uint16_t*)y;
+    a.status = status;
+    a.R = R;
+    a.T = d.T;
+    a.H = d.H;
+    a.F = F;
+    a.K = d.K;
+    a.E = d.E;
+    a.apply = apply_probs;
+    hipLaunchKernelGGL(k_decode_reset, dim3(1), dim3(256), 0, s, a.ctl, kCtlInts, status);
+    if (d.T == 0) return hipGetLastError();   // nothing to compute: no launch of the layer
+    // two workgroups per CU (the fp8 units hold about 190 registers), a whole
+    // number of workgroups per queue
+    int grid = 2 * num_cu;
+    grid = (grid + kQueues - 1) / kQueues * kQueues;
+    hipLaunchKernelGGL(k_decode_layer, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

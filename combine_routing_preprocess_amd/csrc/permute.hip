@@ -23,10 +23,12 @@
 // kernel.  Row reads are ordinary loads: measured on MI355X, non-temporal
 // loads in this read-once / write-k pattern cost about a fifth of the rate.
 // fp8 rows carry their per-128-column fp32 scales along (slice 0).
-#include "moe_internal.h"
+#include "device_ops.h"
 
 namespace moe {
 namespace {
+
+using namespace ops;
 
 constexpr int kPermU = 1;   // 16-byte chunks held per lane per pass
 constexpr int kPermSlice = 64;   // chunks per wavefront (one 1 KB piece)
@@ -71,71 +73,16 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
     }
 }
 
-// Quantise-on-dispatch: bf16 token rows -> e4m3 codes + 1x128 fp32 scales,
-// written to every kept copy's row.  One wavefront per (token, group of 8
-// column blocks of 128); 16 lanes per block, 8 values per lane, 4 blocks per
-// step.  The block scale and codes follow the same rule as the expert MLP's
-// row quantiser (amax / 448, nearest-even codes saturating at 448), so rows
-// quantised here feed the fp8 expert GEMMs unchanged.
-constexpr int kPQBlocks = 8;
-
 __global__ __launch_bounds__(256) void k_permute_quant(const uint16_t* __restrict__ x, int H, int T, int K, int R,
                                                        const int32_t* __restrict__ row_id, uint8_t* __restrict__ out,
                                                        float* __restrict__ outs) {
-    constexpr int NIT = kPQBlocks / 4;
     const int lane = threadIdx.x & 63;
     const int nb = H / 128;
     const int ngrp = (nb + kPQBlocks - 1) / kPQBlocks;
     const long long wv = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const long long t = wv / ngrp;
     if (t >= T) return;
-    const int b0 = (int)(wv - t * ngrp) * kPQBlocks;
-    const int g = lane >> 4, l16 = lane & 15;
-    const uint16_t* src = x + (size_t)t * H;
-    float v[NIT][8];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int b = b0 + 4 * it + g;
-        if (b < nb) {
-            const u32x4 w = *(const u32x4*)(src + (size_t)b * 128 + l16 * 8);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[it][2 * i] = bf16_lo(w[i]);
-                v[it][2 * i + 1] = bf16_hi(w[i]);
-            }
-        }
-    }
-    u32x2 code[NIT];
-    float sc[NIT];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-        const int b = b0 + 4 * it + g;
-        if (b < nb) {                       // whole 16-lane groups are active or not
-            float amax = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[it][i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            amax = fmaxf(amax, __shfl_xor(amax, 4));
-            amax = fmaxf(amax, __shfl_xor(amax, 8));
-            sc[it] = e4m3_scale(amax);
-            code[it][0] = e4m3_pack4(v[it][0], v[it][1], v[it][2], v[it][3], sc[it]);
-            code[it][1] = e4m3_pack4(v[it][4], v[it][5], v[it][6], v[it][7], sc[it]);
-        }
-    }
-    const int32_t* rid = row_id + (size_t)t * K;
-    for (int j = 0; j < K; ++j) {
-        const int r = rid[j];
-        if (r < 0 || r >= R) continue;
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            const int b = b0 + 4 * it + g;
-            if (b < nb) {
-                __builtin_nontemporal_store(code[it], (u32x2*)(out + (size_t)r * H + (size_t)b * 128 + l16 * 8));
-                if (l16 == 0) outs[(size_t)r * nb + b] = sc[it];
-            }
-        }
-    }
+    permute_quant_wave(x, H, K, R, row_id, out, outs, t, (int)(wv - t * ngrp) * kPQBlocks, lane);
 }
 
 }  // namespace

@@ -310,6 +310,36 @@ int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_pro
 int moe_combine_fp8(const moe_handle* h, const void* d_expert_out_q, const float* d_expert_out_scales,
                     int32_t apply_probs, void* d_y, void* stream);
 
+/* ---- persistent decode layer ----------------------------------------------------
+ * [P5] first commit message (dispatch, FC1, FC2 and combine fused in one kernel
+ * for decode, stages handing work to each other through flags instead of
+ * separate launches) and review-fix commit (live-token trim; an empty batch
+ * launches nothing that computes).  After moe_route_preprocess on the handle,
+ * one call runs the rest of the layer with fp8 weights: quantise-on-dispatch
+ * of the bf16 token rows (as moe_permute_quantize), FC1 + SwiGLU, the 1x128
+ * re-quantisation of the activations, FC2 into d_expert_out, and the combine
+ * into d_y (as moe_combine), as one persistent kernel after a small reset of
+ * its control block.  Work items are handed out by device-side queues and
+ * wait on the items they depend on; the result is bit-identical to
+ * moe_permute_quantize + moe_grouped_swiglu_mlp (fp8) + moe_combine.
+ *   Requires desc.payload = MOE_BF16, H and F multiples of 128.
+ *   d_x            [T,H] bf16 tokens
+ *   d_w1, d_w1_scales, d_w2, d_w2_scales  as moe_grouped_swiglu_mlp, fp8
+ *   d_scratch      >= moe_decode_layer_scratch_bytes(h, F) bytes
+ *   d_expert_out   [R,H] bf16, caller-owned and reused; rows holding no kept
+ *                  copy are unspecified
+ *   d_y            [T,H] bf16 out
+ *   d_status       [1] int32 out, written fresh: 0, or bit 0 set if a wait of
+ *                  the kernel ran past its bound (0.25 s) and the outputs are
+ *                  then unspecified; the kernel always runs to its end.
+ * Currently switched off: after all argument checks it returns
+ * MOE_EUNSUPPORTED and enqueues nothing (its first run on an MI355X did not
+ * finish, with no cause shown yet). */
+size_t moe_decode_layer_scratch_bytes(const moe_handle* h, int32_t F);
+int moe_decode_layer_fp8(const moe_handle* h, int32_t F, const void* d_x, const void* d_w1, const float* d_w1_scales,
+                         const void* d_w2, const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
+                         void* d_expert_out, int32_t apply_probs, void* d_y, int32_t* d_status, void* stream);
+
 /* ---- backward (gradients of dispatch and combine) ---------------------------
  * [P2] "Full HybridEP reference validation" (hidden-state and probability
  * gradients of the backward-of-dispatch and of the backward-of-combine), [P3]

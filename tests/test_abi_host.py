@@ -329,3 +329,33 @@ def test_noalloc_mlp_rejects_sizes_beyond_its_array_on_the_host():
                                             None) == A.MOE_EINVAL
     assert L.moe_grouped_swiglu_mlp_noalloc(C.byref(h), 2048, A.BF16, x, None, x, None, x, None,
                                             C.c_void_p(base + 8), None) == A.MOE_EALIGN
+
+
+def test_decode_layer_argument_checks_before_launch():
+    """moe_decode_layer_fp8 refuses bad arguments before any device call."""
+    L = A.lib()
+    d = _desc(T=16, H=256, E=8, K=2, pad_multiple=16)
+    rc, h, base, n, _buf = _host_handle(d)
+    assert rc == 0
+    x = C.c_void_p(base)
+    need = L.moe_decode_layer_scratch_bytes(C.byref(h), 256)
+    assert need >= L.moe_mlp_scratch_bytes(C.byref(h), 256, A.FP8E4M3_B128)
+    assert L.moe_decode_layer_scratch_bytes(C.byref(h), 100) == 0
+    call = lambda **kw: L.moe_decode_layer_fp8(
+        C.byref(h), kw.get("F", 256), kw.get("x", x), kw.get("w1", x), kw.get("w1s", x), kw.get("w2", x),
+        kw.get("w2s", x), kw.get("scr", x), kw.get("nbytes", need), kw.get("eo", x), 1, kw.get("y", x),
+        kw.get("st", x), None)
+    assert call() == A.MOE_ESTALE                     # no routing metadata yet
+    h.state = 1                                        # every case below fails before any device call
+    assert call(F=100) == A.MOE_ESHAPE
+    assert call(w1=None) == A.MOE_EINVAL
+    assert call(st=None) == A.MOE_EINVAL
+    assert call(y=None) == A.MOE_EINVAL
+    assert call(w2=C.c_void_p(base + 8)) == A.MOE_EALIGN
+    assert call(st=C.c_void_p(base + 2)) == A.MOE_EALIGN
+    assert call(nbytes=need - 1) == A.MOE_ENOSPC
+    assert call() == A.MOE_EUNSUPPORTED               # switched off: nothing is launched
+    d8 = _desc(T=16, H=256, E=8, K=2, payload="fp8")
+    rc, h8, base8, n8, _buf8 = _host_handle(d8)
+    h8.state = 1
+    assert L.moe_decode_layer_fp8(C.byref(h8), 256, x, x, x, x, x, x, 1 << 30, x, 1, x, x, None) == A.MOE_EDTYPE

@@ -138,3 +138,121 @@ def test_decode_graph_replay_matches_eager(fp8_weights):
             torch.cuda.synchronize()
             assert torch.equal(replay.view(torch.int16), yb.view(torch.int16)), (bucket, rep)
             assert int(d.flag.item()) == 0
+
+
+MEGA_OFF = pytest.mark.skip(reason="persistent decode layer switched off: its first MI355X run (16 tokens) did not "
+                                  "finish within minutes and no cause has been shown; moe_decode_layer_fp8 returns "
+                                  "MOE_EUNSUPPORTED")
+
+
+def _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, scratch=None):
+    """preprocess + the persistent decode layer; returns (y, expert_out, status)."""
+    scratch = scratch if scratch is not None else torch.empty(d.decode_layer_scratch_bytes(c.F), dtype=torch.uint8,
+                                                              device=DEV)
+    eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((d.T, c.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    st = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    d.preprocess(dev(idx), dev(pr), tl)
+    d.decode_layer_fp8(dev(x), w1q, w2q, w1s, w2s, scratch=scratch, expert_out=eo, out=y, status=st)
+    return y, eo, st
+
+
+@MEGA_OFF
+@pytest.mark.parametrize("T", [16, 64, 100, 256])
+def test_decode_megakernel_matches_separate_launches_and_oracle(fp8_weights, T):
+    """The persistent decode layer (quantise-on-dispatch, FC1, activation
+    quantiser, FC2, combine in one launch) equals the separate launches bit
+    for bit, and every live token agrees with the oracle."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    bucket, idx, pr, x = _decode_case(c, T)
+    log("decode megakernel", T, bucket)
+    tl = torch.tensor([T], dtype=torch.int32, device=DEV)
+    d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    y, eo, st = _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s)
+    d2 = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    y2 = d2.layer(dev(x), dev(idx), dev(pr), w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    rt = oracle.route(idx, 0, c.E, c.K, pr, c.pad, -1, d.R, T)
+    want = oracle.layer_tokens(list(range(T)), x, rt, lambda e, rows: oracle.expert_mlp_fp8(
+        rows, w1q[e].cpu().numpy(), w1s[e].cpu().numpy(), w2q[e].cpu().numpy(), w2s[e].cpu().numpy()))
+    _check(host_bf16(y[:T]), want, f"megakernel T {T}")
+    if T < bucket:
+        assert torch.count_nonzero(y[T:].float()).item() == 0
+
+
+@MEGA_OFF
+def test_decode_megakernel_graph_replay_and_empty_batch(fp8_weights):
+    """preprocess + the persistent decode layer captured once per bucket and
+    replayed with new inputs (live counts bucket, half, 1 and 0): every replay
+    equals the eager run bit for bit with a clear status word."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    for bucket in (16, 64):
+        log("decode megakernel graph", bucket)
+        d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+        _, idx, pr, x = _decode_case(c, bucket)
+        xb, rb, pb = dev(x).view(torch.bfloat16), dev(idx), dev(pr)
+        tl = torch.tensor([bucket], dtype=torch.int32, device=DEV)
+        scr = torch.empty(d.decode_layer_scratch_bytes(c.F), dtype=torch.uint8, device=DEV)
+        eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+        yb = torch.empty((bucket, c.H), dtype=torch.bfloat16, device=DEV)
+        st = torch.empty(1, dtype=torch.int32, device=DEV)
+
+        def step():
+            d.preprocess(rb, pb, tl)
+            d.decode_layer_fp8(xb, w1q, w2q, w1s, w2s, scratch=scr, expert_out=eo, out=yb, status=st)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for rep, T in enumerate((bucket, bucket // 2 + 1, 1, 0)):
+            _, idx, pr, x = _decode_case(c, bucket)
+            rb.copy_(dev(np.roll(idx, rep + 1, axis=0)))
+            pb.copy_(dev(pr))
+            xb.copy_(dev(x).view(torch.bfloat16))
+            tl.fill_(T)
+            g.replay()
+            torch.cuda.synchronize()
+            assert int(st.item()) == 0, (bucket, rep)
+            replay = yb.clone()
+            step()
+            torch.cuda.synchronize()
+            assert int(st.item()) == 0
+            assert torch.equal(replay.view(torch.int16), yb.view(torch.int16)), (bucket, rep)
+            if T == 0:
+                assert torch.count_nonzero(yb.float()).item() == 0
+
+
+@MEGA_OFF
+@pytest.mark.parametrize("T,H,E,K,F,pad", [(33, 256, 8, 2, 256, 16), (1, 128, 4, 1, 128, 1), (70, 384, 5, 3, 128, 8)])
+def test_decode_megakernel_small_shapes(T, H, E, K, F, pad):
+    """Small shapes, ragged expert counts: bit-identical to the separate
+    launches, and against the oracle."""
+    idx, pr = S.route_softmax_topk(T, E, K, 40 + T)
+    x = S.bf16_normal((T, H), 41 + T)
+    w1q, w1s = S.weights_fp8_blocks(E, 2 * F, H, 42, std=0.05)
+    w2q, w2s = S.weights_fp8_blocks(E, H, F, 43, std=0.05)
+    W = [t.to(DEV) for t in (w1q, w1s, w2q, w2s)]
+    log("decode megakernel small", T, H, E, K, F, pad)
+    d = Dispatcher(T, H, E, K, pad_multiple=pad)
+    scr = torch.empty(d.decode_layer_scratch_bytes(F), dtype=torch.uint8, device=DEV)
+    eo = torch.empty((d.R, H), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    st = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    d.preprocess(dev(idx), dev(pr))
+    d.decode_layer_fp8(dev(x), W[0], W[2], W[1], W[3], scratch=scr, expert_out=eo, out=y, status=st)
+    d2 = Dispatcher(T, H, E, K, pad_multiple=pad)
+    y2 = d2.layer(dev(x), dev(idx), dev(pr), W[0], W[2], w1_scales=W[1], w2_scales=W[3])
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    rt = oracle.route(idx, 0, E, K, pr, pad, -1, d.R)
+    want = oracle.layer_tokens(np.arange(T), x, rt, lambda e, rows: oracle.expert_mlp_fp8(
+        rows, w1q[e].numpy(), w1s[e].numpy(), w2q[e].numpy(), w2s[e].numpy()))
+    _check(host_bf16(y), want, "megakernel small")
