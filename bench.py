@@ -84,6 +84,8 @@ def main() -> int:
     ap.add_argument("--workload", choices=("dsv3_layer", "decode"), default="dsv3_layer",
                     help="decode: only the fp8 decode layer, eager, for kernel profiling")
     ap.add_argument("--tokens", type=int, default=16, help="decode workload: live tokens (bucket = next pow2)")
+    ap.add_argument("--decode-path", choices=("separate", "fused"), default="separate",
+                    help="decode workload: separate launches or the fused decode layer")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -515,9 +517,16 @@ def run_decode(args):
     eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
 
-    def step():
-        d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, scratch=scr, expert_out=eo, out=y,
-                T_live=tl, check_overflow=True)
+    if args.decode_path == "fused":
+        scr = torch.empty(d.decode_fused_scratch_bytes(c.F), dtype=torch.uint8, device=dev)
+
+        def step():
+            d.preprocess(rt, pt, tl)
+            d.decode_fused_fp8(x, w1q, w2q, w1s, w2s, scratch=scr, expert_out=eo, out=y)
+    else:
+        def step():
+            d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, scratch=scr, expert_out=eo,
+                    out=y, T_live=tl, check_overflow=True)
 
     _require_clear_flag(d, rt, pt, tl)
     for _ in range(args.warmup):
@@ -529,7 +538,8 @@ def run_decode(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     print(json.dumps({"workload": f"decode_fp8: {T_live} live tokens (bucket {T}) x {c.H}, {c.E} experts top-{c.K}, "
-                                  f"FFN {c.F}, fp8 e4m3 weights", "ms_per_layer_eager": round(ms, 4),
+                                  f"FFN {c.F}, fp8 e4m3 weights", "path": args.decode_path,
+                      "ms_per_layer_eager": round(ms, 4),
                       "steps": args.steps}), flush=True)
     return 0
 
@@ -667,11 +677,29 @@ def run_workloads():
         gm, gmed = _graph_times(step)
         touched = int((oracle.route(idx, 0, c.E, c.K, pr, c.pad)["counts"] > 0).sum())
         wbytes = touched * per_expert
+        # the fused decode layer: preprocess + quantise-on-dispatch + one persistent kernel
+        df = Dispatcher(T, c.H, c.E, c.K, pad_multiple=c.pad)
+        fscr = torch.empty(df.decode_fused_scratch_bytes(c.F), dtype=torch.uint8, device=dev)
+        feo = torch.empty((df.R, c.H), dtype=torch.bfloat16, device=dev)
+        fy = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
+
+        def fstep():
+            df.preprocess(rt, pt)
+            df.decode_fused_fp8(x, w1q, w2q, w1s, w2s, scratch=fscr, expert_out=feo, out=fy)
+
+        fm, fmed = _graph_times(fstep)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(fy.view(torch.int16), y.view(torch.int16)))
         out5[f"T{T}"] = {"graph_min_ms": round(gm, 4), "graph_median_ms": round(gmed, 4),
                          "tokens_per_s": round(T / (gm * 1e-3), 1), "experts_touched": touched,
                          "weight_bytes": wbytes, "weight_GB_s": round(wbytes / (gm * 1e-3) / 1e9, 1),
-                         "frac_of_hbm_roofline": round(wbytes / (gm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        del d, perm, scr, eo, y
+                         "frac_of_hbm_roofline": round(wbytes / (gm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "fused": {"graph_min_ms": round(fm, 4), "graph_median_ms": round(fmed, 4),
+                                   "tokens_per_s": round(T / (fm * 1e-3), 1),
+                                   "weight_GB_s": round(wbytes / (fm * 1e-3) / 1e9, 1),
+                                   "frac_of_hbm_roofline": round(wbytes / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "bit_identical_to_separate": same}}
+        del d, perm, scr, eo, y, df, fscr, feo, fy
     res["decode_fp8_7168_e256"] = out5
     del w1q, w1s, w2q, w2s
     torch.cuda.empty_cache()

@@ -73,6 +73,9 @@ SIGNATURES = [
     ("moe_decode_layer_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32]),
     ("moe_decode_layer_fp8", C.c_int, [C.POINTER(MoeHandle), C.c_int32, _P, _P, _P, _P, _P, _P, C.c_size_t, _P,
                                        C.c_int32, _P, _P, _P]),
+    ("moe_decode_fused_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32]),
+    ("moe_decode_fused_fp8", C.c_int, [C.POINTER(MoeHandle), C.c_int32, _P, _P, _P, _P, _P, _P, C.c_size_t, _P,
+                                       C.c_int32, _P, _P]),
     ("moe_dispatch_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, _P, _P, _P]),
     ("moe_combine_backward", C.c_int, [C.POINTER(MoeHandle), _P, _P, C.c_int32, _P, _P, _P]),
 ]

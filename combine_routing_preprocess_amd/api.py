@@ -487,6 +487,34 @@ class Dispatcher:
                 "moe_decode_layer_fp8")
         return out
 
+    def decode_fused_scratch_bytes(self, F: int) -> int:
+        return int(A.lib().moe_decode_fused_scratch_bytes(C.byref(self.h), int(F)))
+
+    def decode_fused_fp8(self, x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor, w1_scales: torch.Tensor,
+                         w2_scales: torch.Tensor, *, scratch: torch.Tensor, expert_out: torch.Tensor,
+                         out: torch.Tensor, apply_probs: bool = True) -> torch.Tensor:
+        """The rest of the layer after preprocess(), with fp8 weights, in two
+        launches: quantise-on-dispatch, then one persistent kernel for FC1 +
+        SwiGLU, the activation blocks, FC2 into ``expert_out`` and the combine
+        into ``out``."""
+        _need(self.payload == A.BF16, "the decode layer takes bf16 token rows")
+        self._check_x(x)
+        F, wdtype = self._check_w1(w1, w1_scales)
+        F2, wdtype2 = self._check_w2(w2, w2_scales)
+        _need(wdtype == "fp8" and wdtype2 == "fp8" and F2 == F, "the decode layer takes fp8 w1 and w2 of one FFN width")
+        self._dev(scratch, "scratch")
+        need = self.decode_fused_scratch_bytes(F)
+        _need(need > 0, "the fused decode layer needs H, F multiples of 128 and H <= 8192")
+        _need(scratch.numel() * scratch.element_size() >= need, f"scratch holds fewer than the {need} bytes needed")
+        self._check_expert_out(expert_out)
+        self._dev(out, "out")
+        _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (self.T, self.H), "out must be bf16 [T,H]")
+        A.check(A.lib().moe_decode_fused_fp8(C.byref(self.h), F, _ptr(x), _ptr(w1), _ptr(w1_scales), _ptr(w2),
+                                             _ptr(w2_scales), _ptr(scratch), scratch.numel() * scratch.element_size(),
+                                             _ptr(expert_out), 1 if apply_probs else 0, _ptr(out), _stream()),
+                "moe_decode_fused_fp8")
+        return out
+
     def layer(self, x, routing, probs, w1, w2, *, perm=None, scratch=None, expert_out=None, out=None,
               w1_scales=None, w2_scales=None, T_live=None, apply_probs=True, check_overflow=False):
         """dispatch -> grouped MLP -> combine on the current stream.  With

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libmoe_route.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "ring.cpp", "route.hip", "permute.hip", "combine.hip", "backward.hip", "gemm_bf16.hip", "gemm_fp8.hip", "noalloc.hip", "decode.hip"]
+SOURCES = ["api.cpp", "ring.cpp", "route.hip", "permute.hip", "combine.hip", "backward.hip", "gemm_bf16.hip", "gemm_fp8.hip", "noalloc.hip", "decode.hip", "decode_fused.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),

@@ -407,6 +407,32 @@ int moe_decode_layer_fp8(const moe_handle* h, int32_t F, const void* d_x, const 
                                       apply_probs ? 1 : 0, d_y, d_status, ncu, (hipStream_t)stream));
 }
 
+size_t moe_decode_fused_scratch_bytes(const moe_handle* h, int32_t F) {
+    if (!h || F <= 0 || !decode_fused_shape_ok(h->desc.H, F)) return 0;
+    const moe_desc& d = h->desc;
+    return up(decode_fused_scratch_bytes((long long)d.out_rows, d.T, d.K, d.H, F, d.E), kAlign);
+}
+
+int moe_decode_fused_fp8(const moe_handle* h, int32_t F, const void* d_x, const void* d_w1, const float* d_w1_scales,
+                         const void* d_w2, const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
+                         void* d_expert_out, int32_t apply_probs, void* d_y, void* stream) {
+    int rc = check_handle(h, true);
+    if (rc) return rc;
+    const moe_desc& d = h->desc;
+    if (d.payload != MOE_BF16) return MOE_EDTYPE;             // token rows are bf16, quantised here
+    if (F <= 0 || !decode_fused_shape_ok(d.H, F)) return MOE_ESHAPE;
+    if (!d_w1 || !d_w1_scales || !d_w2 || !d_w2_scales || !d_scratch) return MOE_EINVAL;
+    if (d.T > 0 && (!d_x || !d_expert_out || !d_y)) return MOE_EINVAL;
+    if (!al16(d_w1) || !al16(d_w2) || !al4(d_w1_scales) || !al4(d_w2_scales) || !al16(d_scratch))
+        return MOE_EALIGN;
+    if ((d_x && !al16(d_x)) || (d_expert_out && !al16(d_expert_out)) || (d_y && !al16(d_y))) return MOE_EALIGN;
+    if (scratch_bytes < moe_decode_fused_scratch_bytes(h, F)) return MOE_ENOSPC;
+    const int ncu = num_cu();
+    if (ncu <= 0) return MOE_EHIP;
+    return hip_rc(launch_decode_fused(h, F, d_x, d_w1, d_w1_scales, d_w2, d_w2_scales, d_scratch, d_expert_out,
+                                      apply_probs ? 1 : 0, d_y, ncu, (hipStream_t)stream));
+}
+
 int moe_combine(const moe_handle* h, const void* d_expert_out, int32_t apply_probs, void* d_y,
                 void* stream) {
     int rc = check_handle(h, true);

@@ -76,6 +76,9 @@ __device__ __forceinline__ void quant_row_wave(const SRC* __restrict__ src, int 
     }
 }
 
+// SwiGLU of one feature: silu(gate) * up.
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + __expf(-g)) * u; }
+
 // The 32 operand bytes of a lane in a 128-wide K block: bytes kq..kq+15 and
 // kq+64..kq+79 with kq = 16*(lane/16).  Weights and tokens use the same K
 // assignment, so each 128-byte block is covered exactly once, and one load
@@ -155,7 +158,7 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float g = acc_g[t][i], u = acc_u[t][i];
-                a[i] = g / (1.f + __expf(-g)) * u;
+                a[i] = swiglu(g, u);
             }
             o.x = a[0]; o.y = a[1]; o.z = a[2]; o.w = a[3];
             *(float4*)((float*)Outv + orow) = o;

@@ -95,6 +95,11 @@ size_t fp8_mlp_scratch_bytes(long long R, int H, int F);
 // persistent decode layer (quantise-on-dispatch, FC1, activation quantiser,
 // FC2, combine in one launch after a control-block reset)
 size_t decode_layer_scratch_bytes(long long R, int H, int F);
+size_t decode_fused_scratch_bytes(long long R, int T, int K, int H, int F, int E);
+bool decode_fused_shape_ok(int H, int F);
+hipError_t launch_decode_fused(const moe_handle* h, int F, const void* x, const void* w1, const float* w1s,
+                               const void* w2, const float* w2s, void* scratch, void* expert_out, int apply_probs,
+                               void* y, int num_cu, hipStream_t s);
 hipError_t launch_decode_layer(const moe_handle* h, int F, const void* x, const void* w1, const float* w1s,
                                const void* w2, const float* w2s, void* scratch, void* expert_out, int apply_probs,
                                void* y, int32_t* status, int num_cu, hipStream_t s);

@@ -340,6 +340,39 @@ int moe_decode_layer_fp8(const moe_handle* h, int32_t F, const void* d_x, const 
                          const void* d_w2, const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
                          void* d_expert_out, int32_t apply_probs, void* d_y, int32_t* d_status, void* stream);
 
+/* ---- fused decode layer ------------------------------------------------------------
+ * [P5] first commit message (dispatch, FC1, FC2 and combine of a decode batch
+ * fused into one persistent kernel with block-scaled low-precision expert
+ * weights) and review-fix commit (work trimmed to the live tokens; an empty
+ * batch launches nothing).  After moe_route_preprocess on the handle, one call
+ * runs the rest of the layer with fp8 weights in two launches: a small one
+ * that quantises every token row into its kept copies (as
+ * moe_permute_quantize), zeroes the output rows of tokens without a kept copy
+ * and clears the completion counters; then one persistent kernel whose work
+ * units are (touched expert, 128-feature slice of the FFN).  A unit computes
+ * FC1 + SwiGLU for its slice, quantises the slice as one 1x128 activation
+ * block, and adds its FC2 share through a partial buffer; the last unit of an
+ * expert reduces the expert's rows into d_expert_out, and the last expert of a
+ * token combines the token into d_y.  No work unit waits for another.  The
+ * result is bit-identical to moe_permute_quantize + moe_grouped_swiglu_mlp
+ * (fp8) + moe_combine on the same handle.
+ *   Requires desc.payload = MOE_BF16, H and F multiples of 128, H <= 8192
+ *   (MOE_ESHAPE otherwise).
+ *   d_x            [T,H] bf16 tokens
+ *   d_w1, d_w1_scales, d_w2, d_w2_scales  as moe_grouped_swiglu_mlp, fp8
+ *   d_scratch      >= moe_decode_fused_scratch_bytes(h, F) bytes (token codes
+ *                  per row, FC2 partials [F/128, T*K, H] fp32, counters);
+ *                  contents on entry are ignored
+ *   d_expert_out   [R,H] bf16, caller-owned and reused; rows holding no kept
+ *                  copy are not written
+ *   d_y            [T,H] bf16 out
+ * Two calls that share d_scratch must not overlap.  Returns MOE_ENOSPC if the
+ * scratch is too small; nothing is enqueued on any error. */
+size_t moe_decode_fused_scratch_bytes(const moe_handle* h, int32_t F);
+int moe_decode_fused_fp8(const moe_handle* h, int32_t F, const void* d_x, const void* d_w1, const float* d_w1_scales,
+                         const void* d_w2, const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
+                         void* d_expert_out, int32_t apply_probs, void* d_y, void* stream);
+
 /* ---- backward (gradients of dispatch and combine) ---------------------------
  * [P2] "Full HybridEP reference validation" (hidden-state and probability
  * gradients of the backward-of-dispatch and of the backward-of-combine), [P3]

@@ -331,6 +331,43 @@ def test_noalloc_mlp_rejects_sizes_beyond_its_array_on_the_host():
                                             C.c_void_p(base + 8), None) == A.MOE_EALIGN
 
 
+def test_decode_fused_argument_checks_before_launch():
+    """moe_decode_fused_fp8 refuses bad arguments before any device call, and
+    its scratch covers the FC2 partials of every copy."""
+    L = A.lib()
+    d = _desc(T=16, H=256, E=8, K=2, pad_multiple=16)
+    rc, h, base, n, _buf = _host_handle(d)
+    assert rc == 0
+    x = C.c_void_p(base)
+    need = L.moe_decode_fused_scratch_bytes(C.byref(h), 256)
+    assert need >= (256 // 128) * 16 * 2 * 256 * 4          # [F/128, T*K, H] fp32 partials
+    assert L.moe_decode_fused_scratch_bytes(C.byref(h), 100) == 0
+    call = lambda **kw: L.moe_decode_fused_fp8(
+        C.byref(kw.get("h", h)), kw.get("F", 256), kw.get("x", x), kw.get("w1", x), kw.get("w1s", x),
+        kw.get("w2", x), kw.get("w2s", x), kw.get("scr", x), kw.get("nbytes", need), kw.get("eo", x), 1,
+        kw.get("y", x), None)
+    assert call() == A.MOE_ESTALE                     # no routing metadata yet
+    h.state = 1                                        # every case below fails before any device call
+    assert call(F=100) == A.MOE_ESHAPE
+    assert call(w1=None) == A.MOE_EINVAL
+    assert call(w2s=None) == A.MOE_EINVAL
+    assert call(y=None) == A.MOE_EINVAL
+    assert call(eo=None) == A.MOE_EINVAL
+    assert call(w2=C.c_void_p(base + 8)) == A.MOE_EALIGN
+    assert call(w1s=C.c_void_p(base + 2)) == A.MOE_EALIGN
+    assert call(nbytes=need - 1) == A.MOE_ENOSPC
+    dw = _desc(T=16, H=8320, E=8, K=2)                 # H / 128 = 65 K blocks: past the kernel's limit
+    rc, hw, basew, nw, _bufw = _host_handle(dw)
+    assert rc == 0
+    hw.state = 1
+    assert L.moe_decode_fused_scratch_bytes(C.byref(hw), 256) == 0
+    assert call(h=hw) == A.MOE_ESHAPE
+    d8 = _desc(T=16, H=256, E=8, K=2, payload="fp8")
+    rc, h8, base8, n8, _buf8 = _host_handle(d8)
+    h8.state = 1
+    assert call(h=h8, nbytes=1 << 30) == A.MOE_EDTYPE
+
+
 def test_decode_layer_argument_checks_before_launch():
     """moe_decode_layer_fp8 refuses bad arguments before any device call."""
     L = A.lib()

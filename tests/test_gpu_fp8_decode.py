@@ -256,3 +256,134 @@ def test_decode_megakernel_small_shapes(T, H, E, K, F, pad):
     want = oracle.layer_tokens(np.arange(T), x, rt, lambda e, rows: oracle.expert_mlp_fp8(
         rows, w1q[e].numpy(), w1s[e].numpy(), w2q[e].numpy(), w2s[e].numpy()))
     _check(host_bf16(y), want, "megakernel small")
+
+
+# ---- fused decode layer (quantise-on-dispatch launch + one persistent kernel) ----
+
+def _fused_run(d, x, idx, pr, tl, w1, w1s, w2, w2s, F, H):
+    """preprocess + the fused decode layer on fresh buffers; returns (y, expert_out)."""
+    scratch = torch.empty(d.decode_fused_scratch_bytes(F), dtype=torch.uint8, device=DEV)
+    scratch.fill_(0xA5)                                # the call must not depend on scratch contents
+    eo = torch.zeros((d.R, H), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((d.T, H), 7.0, dtype=torch.bfloat16, device=DEV)
+    d.preprocess(dev(idx), dev(pr), tl)
+    d.decode_fused_fp8(dev(x), w1, w2, w1s, w2s, scratch=scratch, expert_out=eo, out=y)
+    return y, eo
+
+
+def _separate_run(d, x, idx, pr, tl, w1, w1s, w2, w2s):
+    """The same layer as separate launches: dispatch, fp8 grouped MLP, combine."""
+    perm, *_ = d.dispatch(dev(x), dev(idx), dev(pr), T_live=tl)
+    eo = d.grouped_mlp(perm, w1, w2, w1_scales=w1s, w2_scales=w2s)
+    y = d.combine(eo)
+    return y, eo
+
+
+def _assert_same_as_separate(d, y, eo, y2, eo2):
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    kept_rows = (d.src_row >= 0).nonzero().flatten()
+    assert torch.equal(eo[kept_rows].view(torch.int16), eo2[kept_rows].view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [16, 64, 100, 256])
+def test_decode_fused_matches_separate_launches_and_oracle(fp8_weights, T):
+    """The fused decode layer in buckets 16, 64, 128 (100 live) and 256:
+    output and expert rows bit-identical to the separate launches, live
+    tokens against the oracle (all of them up to 64, every third above),
+    tokens past the live count exactly zero."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    bucket, idx, pr, x = _decode_case(c, T)
+    log("fused decode", T, bucket)
+    tl = torch.tensor([T], dtype=torch.int32, device=DEV)
+    d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    y, eo = _fused_run(d, x, idx, pr, tl, w1q, w1s, w2q, w2s, c.F, c.H)
+    d2 = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    y2, eo2 = _separate_run(d2, x, idx, pr, tl, w1q, w1s, w2q, w2s)
+    torch.cuda.synchronize()
+    _assert_same_as_separate(d, y, eo, y2, eo2)
+    rt = oracle.route(idx, 0, c.E, c.K, pr, c.pad, -1, d.R, T)
+    toks = list(range(T)) if T <= 64 else list(range(0, T, 3))
+    want = oracle.layer_tokens(toks, x, rt, lambda e, rows: oracle.expert_mlp_fp8(
+        rows, w1q[e].cpu().numpy(), w1s[e].cpu().numpy(), w2q[e].cpu().numpy(), w2s[e].cpu().numpy()))
+    _check(host_bf16(y[toks]), want, f"fused T {T}")
+    if T < bucket:
+        assert torch.count_nonzero(y[T:].float()).item() == 0
+
+
+def test_decode_fused_graph_replay(fp8_weights):
+    """preprocess + the fused decode layer captured once per bucket and
+    replayed with new inputs and live counts (bucket, half, 1, 0): every
+    replay equals the eager run bit for bit; no live token gives all zeros."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    for bucket in (16, 64):
+        log("fused decode graph", bucket)
+        d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+        _, idx, pr, x = _decode_case(c, bucket)
+        xb, rb, pb = dev(x).view(torch.bfloat16), dev(idx), dev(pr)
+        tl = torch.tensor([bucket], dtype=torch.int32, device=DEV)
+        scr = torch.empty(d.decode_fused_scratch_bytes(c.F), dtype=torch.uint8, device=DEV)
+        eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+        yb = torch.empty((bucket, c.H), dtype=torch.bfloat16, device=DEV)
+
+        def step():
+            d.preprocess(rb, pb, tl)
+            d.decode_fused_fp8(xb, w1q, w2q, w1s, w2s, scratch=scr, expert_out=eo, out=yb)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for rep, T in enumerate((bucket, bucket // 2 + 1, 1, 0)):
+            _, idx, pr, x = _decode_case(c, bucket)
+            rb.copy_(dev(np.roll(idx, rep + 1, axis=0)))
+            pb.copy_(dev(pr))
+            xb.copy_(dev(x).view(torch.bfloat16))
+            tl.fill_(T)
+            yb.fill_(3.0)
+            g.replay()
+            torch.cuda.synchronize()
+            replay = yb.clone()
+            yb.fill_(5.0)
+            step()
+            torch.cuda.synchronize()
+            assert torch.equal(replay.view(torch.int16), yb.view(torch.int16)), (bucket, rep)
+            if T == 0:
+                assert torch.count_nonzero(yb.float()).item() == 0
+
+
+@pytest.mark.parametrize("T,H,E,K,F,pad,counts", [
+    (33, 256, 8, 2, 256, 16, None),
+    (1, 128, 4, 1, 128, 1, None),
+    (70, 384, 5, 3, 128, 8, None),                   # > 32 rows per expert: passes of 32 and the rest
+    (67, 256, 5, 1, 256, 4, [0, 1, 16, 17, 33]),     # one and two token blocks, a pass boundary
+])
+def test_decode_fused_small_shapes(T, H, E, K, F, pad, counts):
+    """Small and ragged shapes (a final half stage of W2 rows at H = 128 and
+    384, several passes over an expert's weights): bit-identical to the
+    separate launches, and against the oracle."""
+    if counts is None:
+        idx, pr = S.route_softmax_topk(T, E, K, 40 + T)
+    else:
+        idx = np.repeat(np.arange(E), counts).astype(np.int16)[:, None]
+        idx = idx[np.random.default_rng(T).permutation(T)]
+        pr = np.ones((T, K), np.float32)
+    x = S.bf16_normal((T, H), 41 + T)
+    w1q, w1s = S.weights_fp8_blocks(E, 2 * F, H, 42, std=0.05)
+    w2q, w2s = S.weights_fp8_blocks(E, H, F, 43, std=0.05)
+    W = [t.to(DEV) for t in (w1q, w1s, w2q, w2s)]
+    log("fused decode small", T, H, E, K, F, pad)
+    tl = torch.tensor([T], dtype=torch.int32, device=DEV)
+    d = Dispatcher(T, H, E, K, pad_multiple=pad)
+    y, eo = _fused_run(d, x, idx, pr, tl, W[0], W[1], W[2], W[3], F, H)
+    d2 = Dispatcher(T, H, E, K, pad_multiple=pad)
+    y2, eo2 = _separate_run(d2, x, idx, pr, tl, W[0], W[1], W[2], W[3])
+    torch.cuda.synchronize()
+    _assert_same_as_separate(d, y, eo, y2, eo2)
+    rt = oracle.route(idx, 0, E, K, pr, pad, -1, d.R)
+    want = oracle.layer_tokens(np.arange(T), x, rt, lambda e, rows: oracle.expert_mlp_fp8(
+        rows, w1q[e].numpy(), w1s[e].numpy(), w2q[e].numpy(), w2s[e].numpy()))
+    _check(host_bf16(y), want, "fused small")
