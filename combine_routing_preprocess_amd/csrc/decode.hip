@@ -107,6 +107,7 @@ __device__ __forceinline__ void signal_done(int* c) {
 
 __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
     __shared__ int s_list[kMaxE];    // experts holding rows, ascending
+    __shared__ __attribute__((aligned(16))) unsigned char s_w[4 * kWaveLds];   // weight buffer per wavefront
     __shared__ int s_cnt;
     __shared__ int s_ticket;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
             const int k = i - nD, ai = q + kQueues * (k / upe1), u = k % upe1;
             wait_count(a, ctl + kCtlDispatch, a.T);
             fp8_unit<0>(a.xq, a.xs, a.w1, a.w1s, a.act, a.seg_off, a.kept, a.R, a.H, 2 * a.F, a.F, s_list[ai], u,
-                        lane, wave);
+                        lane, wave, s_w + wave * kWaveLds);
             signal_done(ctl + kCtlFc1 + ai);
         } else if (i < eQ) {
             // Q(a): the expert's activation rows, (row, 8-block group) per wavefront
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
             const int k = i - eQ, ai = q + kQueues * (k / upe2), u = k % upe2;
             wait_count(a, ctl + kCtlQuant + ai, 1);
             fp8_unit<1>(a.aq, a.as, a.w2, a.w2s, a.eo, a.seg_off, a.kept, a.R, a.F, a.H, a.H, s_list[ai], u, lane,
-                        wave);
+                        wave, s_w + wave * kWaveLds);
             signal_done(ctl + kCtlFc2);
         } else {
             // C(t): combine of token t once every FC2 unit is done

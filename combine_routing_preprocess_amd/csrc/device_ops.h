@@ -81,8 +81,8 @@ __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + __
 
 // The 32 operand bytes of a lane in a 128-wide K block: bytes kq..kq+15 and
 // kq+64..kq+79 with kq = 16*(lane/16).  Weights and tokens use the same K
-// assignment, so each 128-byte block is covered exactly once, and one load
-// instruction reads 64 contiguous bytes of each of its 16 rows.
+// assignment, so each 128-byte block is covered exactly once.  Token operands
+// are loaded this way (a few rows, from L2); weights go through wl_load.
 __device__ __forceinline__ i32x8 load_fp8x32(const uint8_t* p) {
     const u32x4 a = *(const u32x4*)p, b = *(const u32x4*)(p + 64);
     return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
@@ -93,16 +93,61 @@ __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
 }
 
+// Weight tiles through a wavefront-private LDS buffer: the loads read whole
+// 128-byte lines (load (u, i) covers rows 8*(i&1) + lane/8 of tile i/2 at K
+// block u, 16 bytes per lane) with the non-temporal policy (weights are read
+// once), the buffer holds them with a 16-byte chunk XOR swizzle, and the MFMA
+// operands are read back from it (lane l: row l%16, chunks l/16 and l/16 + 4).
+// Only this wavefront touches its buffer, and its LDS operations run in
+// order, so no barrier is needed.  Measured on MI355X for the decode layer
+// (7168 x 2048 experts, graph replay): 0.77 -> 0.67 ms at 16 tokens against
+// operand-layout loads that read 64 bytes of each of 16 rows per instruction.
+template <int UU>
+__device__ __forceinline__ void wl_load(const uint8_t* t0, const uint8_t* t1, int Kdim, int kb0, int lane,
+                                        u32x4 (&raw)[UU][4]) {
+#pragma unroll
+    for (int u = 0; u < UU; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            raw[u][i] = __builtin_nontemporal_load((const u32x4*)((i < 2 ? t0 : t1) +
+                                                                  (size_t)(8 * (i & 1) + (lane >> 3)) * Kdim +
+                                                                  (size_t)(kb0 + u) * 128 + 16 * (lane & 7)));
+}
+
+template <int UU>
+__device__ __forceinline__ void wl_stash(unsigned char* lds, int lane, const u32x4 (&raw)[UU][4]) {
+#pragma unroll
+    for (int u = 0; u < UU; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            *(u32x4*)(lds + u * 4096 + r * 128 + 16 * ((lane & 7) ^ (r & 7))) = raw[u][i];
+        }
+}
+
+__device__ __forceinline__ i32x8 wl_operand(const unsigned char* tile, int r, int c1) {
+    const u32x4 lo = *(const u32x4*)(tile + r * 128 + 16 * (c1 ^ (r & 7)));
+    const u32x4 hi = *(const u32x4*)(tile + r * 128 + 16 * ((c1 + 4) ^ (r & 7)));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+constexpr int kWaveLds = kU * 4096;   // bytes of a wavefront's weight buffer
+
 // One pass over up to 16*NTB rows (m0 .. m0+mv-1 of the segment) for this
 // wavefront's two 16-row weight tiles (FC1: gate and up rows of 16 features;
-// FC2: 32 consecutive output rows); NTB token blocks of 16 rows.
+// FC2: 32 consecutive output rows); NTB token blocks of 16 rows.  t0 / t1
+// point at byte 0 of the first row of each tile; lds is this wavefront's
+// kWaveLds-byte buffer.  Per group of kU K blocks the weights are loaded as
+// whole lines, passed through the buffer into operand layout, then
+// multiplied with the token codes (loaded per K block from the quantised
+// rows).
 template <int MODE, int NTB>
 __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const float* __restrict__ Xs,
-                                         const uint8_t* wg, const uint8_t* wu, const float* sg, const float* su,
+                                         const uint8_t* t0, const uint8_t* t1, const float* sg, const float* su,
                                          void* __restrict__ Outv, long long seg, int m0, int mv, int Kdim, int Nout,
-                                         int f0, int lane) {
+                                         int f0, int lane, unsigned char* lds) {
     constexpr int U = kU;
-    const int kq = (lane >> 4) * 16;
+    const int kq = (lane >> 4) * 16, c1 = lane >> 4, r16 = lane & 15;
     const int nkb = Kdim / 128;
     f32x4 acc_g[NTB], acc_u[NTB];
 #pragma unroll
@@ -113,17 +158,20 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
     // token row of this lane in block t: m0 + 16t + lane%16 (clamped)
     size_t xrow[NTB];
 #pragma unroll
-    for (int t = 0; t < NTB; ++t) xrow[t] = (size_t)(seg + m0 + min(16 * t + (lane & 15), mv - 1));
+    for (int t = 0; t < NTB; ++t) xrow[t] = (size_t)(seg + m0 + min(16 * t + r16, mv - 1));
 
     // one group of UU K blocks: the weights of all of them are loaded first
     auto group = [&](int kb0, auto uc) {
         constexpr int UU = decltype(uc)::value;
+        u32x4 raw[UU][4];
+        wl_load<UU>(t0, t1, Kdim, kb0, lane, raw);
+        wl_stash<UU>(lds, lane, raw);
         i32x8 a_g[UU], a_u[UU];
         float s_g[UU], s_u[UU];
 #pragma unroll
         for (int u = 0; u < UU; ++u) {
-            a_g[u] = load_fp8x32(wg + (size_t)(kb0 + u) * 128);
-            a_u[u] = load_fp8x32(wu + (size_t)(kb0 + u) * 128);
+            a_g[u] = wl_operand(lds + u * 4096, r16, c1);
+            a_u[u] = wl_operand(lds + u * 4096, 16 + r16, c1);
             s_g[u] = sg[kb0 + u];
             s_u[u] = su[kb0 + u];
         }
@@ -186,32 +234,31 @@ __device__ __forceinline__ void fp8_unit(const uint8_t* __restrict__ Xq, const f
                                          const uint8_t* __restrict__ W, const float* __restrict__ Ws,
                                          void* __restrict__ Outv, const int64_t* __restrict__ seg_off,
                                          const int32_t* __restrict__ kept, long long R, int Kdim, int Wrows,
-                                         int Nout, int e, int unit, int lane, int wave) {
+                                         int Nout, int e, int unit, int lane, int wave, unsigned char* lds) {
     const long long seg = seg_off[e];
     long long me_l = seg < R ? (long long)kept[e] : 0;
     if (seg + me_l > R) me_l = R - seg;
     const int me = (int)me_l;
     if (me <= 0) return;
 
-    const int kq = (lane >> 4) * 16;                  // this lane's 32 bytes inside a 128 block
     const int nkb = Kdim / 128;
     // first output feature (FC1) / output row (FC2) of this wavefront; its two
     // weight tiles start at rows r0 and r1 (FC1: gate and up rows of features
     // f0..f0+15; FC2: rows f0..f0+15 and f0+16..f0+31, one 128-row scale block)
     const int f0 = MODE == 0 ? unit * kFeat + wave * 16 : unit * kFeat2 + wave * 32;
     const int r0 = f0, r1 = MODE == 0 ? Nout + f0 : f0 + 16;
-    const uint8_t* wg = W + ((size_t)e * Wrows + r0 + (lane & 15)) * Kdim + kq;
-    const uint8_t* wu = W + ((size_t)e * Wrows + r1 + (lane & 15)) * Kdim + kq;
+    const uint8_t* t0 = W + ((size_t)e * Wrows + r0) * Kdim;
+    const uint8_t* t1 = W + ((size_t)e * Wrows + r1) * Kdim;
     const float* sg = Ws + ((size_t)e * (Wrows / 128) + r0 / 128) * nkb;
     const float* su = Ws + ((size_t)e * (Wrows / 128) + r1 / 128) * nkb;
 
     for (int m0 = 0; m0 < me; m0 += 16 * kMaxTB) {
         const int mv = min(16 * kMaxTB, me - m0);
         switch ((mv + 15) / 16) {
-            case 1: fp8_pass<MODE, 1>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
-            case 2: fp8_pass<MODE, 2>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
-            case 3: fp8_pass<MODE, 3>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
-            default: fp8_pass<MODE, 4>(Xq, Xs, wg, wu, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane); break;
+            case 1: fp8_pass<MODE, 1>(Xq, Xs, t0, t1, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane, lds); break;
+            case 2: fp8_pass<MODE, 2>(Xq, Xs, t0, t1, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane, lds); break;
+            case 3: fp8_pass<MODE, 3>(Xq, Xs, t0, t1, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane, lds); break;
+            default: fp8_pass<MODE, 4>(Xq, Xs, t0, t1, sg, su, Outv, seg, m0, mv, Kdim, Nout, f0, lane, lds); break;
         }
     }
 }

@@ -58,10 +58,12 @@ __global__ __launch_bounds__(256) void k_gemm_fp8(const uint8_t* __restrict__ Xq
                                                   void* __restrict__ Outv, const int64_t* __restrict__ seg_off,
                                                   const int32_t* __restrict__ kept, long long R, int Kdim,
                                                   int Wrows, int Nout, int units_per_expert) {
+    __shared__ __attribute__((aligned(16))) unsigned char s_w[4 * kWaveLds];   // one weight buffer per wavefront
     const int e = blockIdx.x / units_per_expert;
     const int unit = blockIdx.x - e * units_per_expert;
-    fp8_unit<MODE>(Xq, Xs, W, Ws, Outv, seg_off, kept, R, Kdim, Wrows, Nout, e, unit, threadIdx.x & 63,
-                   threadIdx.x >> 6);
+    const int wave = threadIdx.x >> 6;
+    fp8_unit<MODE>(Xq, Xs, W, Ws, Outv, seg_off, kept, R, Kdim, Wrows, Nout, e, unit, threadIdx.x & 63, wave,
+                   s_w + wave * kWaveLds);
 }
 
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
