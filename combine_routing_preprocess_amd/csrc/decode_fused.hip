@@ -15,7 +15,7 @@
 //    of every token row into each of its kept copies (codes + 1x128 scales),
 //    zero output rows of tokens without a kept copy, clear the completion
 //    counters, and list the touched experts with compact row offsets.
-//  * k_decode_fused (persistent, one workgroup per CU): work unit = (touched
+//  * k_decode_fused (persistent, two workgroups per CU): work unit = (touched
 //    expert, 128-feature slice s of the FFN).  A unit computes FC1 + SwiGLU
 //    for its 128 features, quantises them as one 1x128 activation block (the
 //    block is whole inside the unit, so no other unit is needed), and
@@ -31,13 +31,15 @@
 //    brings a token's counter to its number of kept copies combines that
 //    token.  Every counter is read only by the workgroup whose increment
 //    returned the final value, after an acquire fence.
-//  * Weights stream into a 4-stage LDS ring by global_load_lds_dwordx4: one
-//    instruction moves 8 whole 128-byte rows (one K block of 8 weight rows),
-//    stored with a 16-byte chunk XOR swizzle so the MFMA operand reads are
-//    conflict-free.  A stage is 256 weight rows x one 128-wide K block
-//    (32 KB): FC1 stages hold the unit's 128 gate and 128 up rows at K block
-//    kb plus the token codes of that block, FC2 stages 256 rows of W2 at the
-//    slice's 128 columns.  Three stages are in flight while one is consumed.
+//  * Four wavefronts per workgroup, two workgroups per CU (while one
+//    synchronises or reduces, the other keeps weights streaming).  FC1:
+//    wavefront w streams the gate and up rows of features 32w..32w+15, then
+//    32w+16..32w+31 of the slice over all K blocks, exactly as the separate
+//    FC1 GEMM does (whole 128-byte lines, non-temporal, through its own LDS
+//    buffer into operand layout).  FC2: wavefront w streams a quarter of the
+//    W2 rows at the slice's 128 columns, eight 16-row tiles (one 128-byte
+//    line per row) per load group.  No barrier runs while weights stream;
+//    the activation block is exchanged through LDS between the two phases.
 //  * v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales: one 128-wide K block
 //    per instruction, weights as A (16 rows) and token or activation codes
 //    as B (16 columns), the same K assignment per lane as the separate fp8
@@ -51,19 +53,14 @@ namespace {
 using namespace ops;
 
 constexpr int kSlice = 128;                  // FFN features per unit
-constexpr int kStRows = 256;                 // weight rows per stage
+constexpr int kWaves = 4;                    // wavefronts per workgroup
 constexpr int kTBMax = 2;                    // token blocks (16 rows) per pass
-constexpr int kRing = 4;                     // stages in the LDS ring
-constexpr int kWBytes = kStRows * 128;       // weight bytes of a stage (32 KB)
-constexpr int kTBytes = kTBMax * 16 * 128;   // token code bytes of a stage
-constexpr int kSlotBytes = kWBytes + kTBytes;
-constexpr int kMaxKB = 64;                   // H / 128 limit (H <= 8192)
-constexpr int kRingBytes = kRing * kSlotBytes;
-constexpr int kXsStride = kMaxKB + 1;                // floats per token row (odd: no bank conflicts)
-constexpr int kXsBytes = kTBMax * 16 * kXsStride * 4; // token scales of a pass
-constexpr int kAqBytes = kTBMax * 16 * 128;           // activation codes of a pass
-constexpr int kWsBytes = 2 * kMaxKB * 4;                // gate and up weight scales of a pass
-constexpr int kLdsBytes = kRingBytes + kXsBytes + kAqBytes + kWsBytes;
+constexpr int kMaxKB = 64;                   // H / 128 and F / 128 limit
+constexpr int kWaveBytes = kWaves * kWaveLds;            // weight buffers of all wavefronts
+constexpr int kAmaxBytes = kWaves * 16 * kTBMax * 4;     // per-wavefront block maxima
+constexpr int kAqBytes = kTBMax * 16 * 128;              // activation codes of a pass
+constexpr int kLdsBytes = kWaveBytes + kAmaxBytes + kAqBytes;
+static_assert(2 * kMaxKB * kMaxKB * 4 <= kWaveBytes, "reduce scales fit the weight buffers");
 
 struct FusedArgs {
     const uint16_t* x;          // [T,H] bf16 tokens
@@ -152,264 +149,176 @@ __global__ __launch_bounds__(256) void k_fused_prep(FusedArgs a) {
     if (threadIdx.x == 0) a.cnt_t[t] = 0;
 }
 
-// ---- LDS DMA ----------------------------------------------------------------
-// One 16-byte-per-lane global -> LDS transfer from a per-lane address; lane
-// l's bytes land at LDS byte address lds + 16*l.  Inline asm, so the compiler
-// does not order later LDS reads after it: completion is awaited explicitly
-// with s_waitcnt vmcnt, counting only these transfers (loads return in issue
-// order, and other memory operations only lengthen a wait).  m0 is written
-// only by these asm statements in this translation unit.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_nt(const void* gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(gptr), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier that waits for this wavefront's LDS operations only (a
-// __syncthreads fence would also wait for the ring transfers in flight).
+// Workgroup barrier that waits for this wavefront's LDS operations only
+// (weight loads of other wavefronts may still be in flight).
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
-}
-
-// 32 operand bytes of row `r` of a swizzled 128-byte-row tile: logical chunks
-// c1 = lane/16 and c1 + 4 (chunk c of row r sits at position c ^ (r & 7)).
-__device__ __forceinline__ i32x8 read_op(const unsigned char* tile, int r, int c1) {
-    const unsigned char* row = tile + r * 128;
-    const u32x4 lo = *(const u32x4*)(row + 16 * (c1 ^ (r & 7)));
-    const u32x4 hi = *(const u32x4*)(row + 16 * ((c1 + 4) ^ (r & 7)));
-    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+// All vector memory operations of this wavefront (its stores) have completed.
+__device__ __forceinline__ void wait_stores() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // One pass of a unit over up to 16*NTB rows of expert e (segment rows m0 ..
-// m0+mv-1), slice s: the FC1 K blocks, the activation block, the FC2 stages.
+// m0+mv-1), slice s: FC1 + SwiGLU of the slice, its activation block, and the
+// FC2 block products of the slice for every output row.
 template <int NTB>
-__device__ __forceinline__ void fused_pass(const FusedArgs& a, unsigned char* smem, int e, int s, long long seg,
-                                           int m0, int mv, int crow, int lane, int wave) {
-    constexpr int NI = 8 + NTB;                 // ring transfers per wavefront per stage
+__device__ __forceinline__ void fused_pass(const FusedArgs& a, const float* __restrict__ w1s, unsigned char* smem,
+                                           int e, int s, long long seg, int m0, int mv, int crow, int lane,
+                                           int wave) {
     const int nkb = a.H / 128;
-    const int nh2 = (a.H + kStRows - 1) / kStRows;
-    const int nst = nkb + nh2;
     const int S = a.F / kSlice;
-    const int c1 = lane >> 4, l16 = lane & 15;
-    unsigned char* ring = smem;
-    float* s_xs = (float*)(smem + kRingBytes);
-    unsigned char* s_aq = smem + kRingBytes + kXsBytes;
-    float* s_ws = (float*)(smem + kRingBytes + kXsBytes + kAqBytes);   // [2][kMaxKB]
-    float* s_amax = (float*)(smem + kLdsBytes);   // [4][16*kTBMax], after the main regions
+    const int c1 = lane >> 4, r16 = lane & 15;
+    unsigned char* wl = smem + wave * kWaveLds;
+    float* s_amax = (float*)(smem + kWaveBytes);
+    unsigned char* s_aq = smem + kWaveBytes + kAmaxBytes;
 
-    lds_barrier();   // the previous pass is done with the ring, token scales and codes
+    lds_barrier();   // the previous pass is done with the activation exchange
 
-    // token scales of the pass: row i (clamped to the last live row) x K block
-    for (int q = threadIdx.x; q < 16 * NTB * nkb; q += 256) {
-        const int i = q / nkb, kb = q - i * nkb;
-        s_xs[i * kXsStride + kb] = a.xs[(size_t)(seg + m0 + min(i, mv - 1)) * nkb + kb];
-    }
-
-    // FC1 weight scales of the slice (gate row block s, up row block F/128 + s),
-    // read here so that no load other than the ring transfers runs in the K loop
-    {
-        const float* sg = a.w1s + ((size_t)e * (2 * (size_t)a.F / 128) + s) * nkb;
-        const float* su = a.w1s + ((size_t)e * (2 * (size_t)a.F / 128) + a.F / 128 + s) * nkb;
-        for (int q = threadIdx.x; q < 2 * nkb; q += 256)
-            s_ws[(q / nkb) * kMaxKB + q % nkb] = q < nkb ? sg[q] : su[q - nkb];
-    }
-
-    // per-lane ring sources.  Weight transfer jj of this wavefront covers
-    // stage rows 64*wave + 8*jj + lane/8, chunk position lane%8 holds chunk
-    // (lane%8) ^ (lane/8) of that row.
-    const int rr = lane >> 3, wc = (lane & 7) ^ rr;
+    // ---- FC1: features 32w + 16hf .. +15 of the slice (hf = 0, 1), gate and up tiles
     const size_t F2 = 2 * (size_t)a.F;
-    const int w1row = (wave < 2 ? s * kSlice + 64 * wave : a.F + s * kSlice + 64 * (wave - 2)) + rr;
-    const uint8_t* p1 = a.w1 + ((size_t)e * F2 + w1row) * a.H + 16 * wc;
-    const uint8_t* p2 = a.w2 + (size_t)e * a.H * a.F + (size_t)s * kSlice + 16 * wc;
-    // token transfer q of this wavefront (lanes 0..31): token rows 16q + 4*wave + lane/8
-    const uint8_t* pt[NTB];
+    const float* sg = w1s + ((size_t)e * (F2 / 128) + s) * nkb;
+    const float* su = w1s + ((size_t)e * (F2 / 128) + a.F / 128 + s) * nkb;
+    float act[2][NTB][4];
 #pragma unroll
-    for (int q = 0; q < NTB; ++q) {
-        const int i = 16 * q + 4 * wave + (rr & 3);
-        pt[q] = a.xq + (size_t)(seg + m0 + min(i, mv - 1)) * a.H + 16 * ((lane & 7) ^ (i & 7));
+    for (int hf = 0; hf < 2; ++hf) {
+        const int f0 = s * kSlice + 32 * wave + 16 * hf;
+        const uint8_t* t0 = a.w1 + ((size_t)e * F2 + f0) * a.H;
+        const uint8_t* t1 = a.w1 + ((size_t)e * F2 + a.F + f0) * a.H;
+        f32x4 acc_g[NTB], acc_u[NTB];
+        fp8_accumulate<NTB>(a.xq, a.xs, t0, t1, sg, su, seg, m0, mv, a.H, lane, wl, acc_g, acc_u);
+#pragma unroll
+        for (int t = 0; t < NTB; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) act[hf][t][i] = swiglu(acc_g[t][i], acc_u[t][i]);
     }
 
-    auto issue = [&](int k) {
-        unsigned char* slot = ring + (k % kRing) * kSlotBytes;
-        const uint32_t wl = lds_addr(slot + 64 * wave * 128);
-        if (k < nkb) {
+    // ---- the slice's 1x128 activation block per token: lane holds token
+    // 16t + l%16, features 32w + 16hf + 4*(l/16) + i of the slice
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) dma16_nt(p1 + (size_t)8 * jj * a.H + (size_t)k * 128, wl + jj * 1024);
-        } else {
-            const int h0 = (k - nkb) * kStRows + 64 * wave + rr;
+    for (int t = 0; t < NTB; ++t) {
+        float m = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                // rows past H (a final half stage) repeat row H-1; their products are not stored
-                const int h = min(h0 + 8 * jj, a.H - 1);
-                dma16_nt(p2 + (size_t)h * a.F, wl + jj * 1024);
-            }
-        }
-        // token codes of K block k (FC2 stages reload block 0: equal transfer counts)
-        const int kt = k < nkb ? k : 0;
-        const uint32_t tl = lds_addr(slot + kWBytes + 4 * wave * 128);
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int q = 0; q < NTB; ++q)
-            if (lane < 32) dma16(pt[q] + (size_t)kt * 128, tl + q * 16 * 128);
-    };
-
-    f32x4 acc[4][NTB];
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(act[hf][t][i]));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (c1 == 0) s_amax[wave * 16 * kTBMax + 16 * t + r16] = m;
+    }
+    lds_barrier();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int t = 0; t < NTB; ++t) {
+        const int tok = 16 * t + r16;
+        float m = s_amax[tok];
 #pragma unroll
-        for (int t = 0; t < NTB; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_amax[w * 16 * kTBMax + tok]);
+        const float sc = e4m3_scale(m);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            *(uint32_t*)(s_aq + tok * 128 + 16 * ((2 * wave + hf) ^ (tok & 7)) + 4 * c1) =
+                e4m3_pack4(act[hf][t][0], act[hf][t][1], act[hf][t][2], act[hf][t][3], sc);
+        if (wave == 0 && c1 == 0 && tok < mv) a.asc[(size_t)(crow + tok) * S + s] = sc;
+    }
+    lds_barrier();
     i32x8 bq[NTB];
+#pragma unroll
+    for (int t = 0; t < NTB; ++t) bq[t] = wl_operand(s_aq, 16 * t + r16, c1);
 
-    for (int k = 0; k < kRing - 1 && k < nst; ++k) issue(k);
-    for (int k = 0; k < nst; ++k) {
-        const int ahead = min(kRing - 2, nst - 1 - k);
-        if (ahead >= 2) wait_vm<2 * NI>();
-        else if (ahead == 1) wait_vm<NI>();
-        else wait_vm<0>();
-        lds_barrier();
-        if (k + kRing - 1 < nst) issue(k + kRing - 1);
-        const unsigned char* slot = ring + (k % kRing) * kSlotBytes;
-        if (k < nkb) {
-            // FC1: gate tiles at stage rows 32w, 32w+16; up tiles at 128+32w, 128+32w+16
-            const float wg = s_ws[k], wu = s_ws[kMaxKB + k];
-            i32x8 xb[NTB];
-            float sx[NTB];
+    // ---- FC2: this wavefront's W2 tiles at the slice's 128 columns, eight
+    // 16-row tiles per load group (tile j of a group at buffer offset 2048j)
+    const int ntiles = a.H / 16;
+    const int per_w = (ntiles + kWaves - 1) / kWaves;
+    const int tb0 = wave * per_w, tb1 = min(ntiles, tb0 + per_w);
+    const uint8_t* w2e = a.w2 + (size_t)e * a.H * a.F + (size_t)s * kSlice + 16 * (lane & 7);
+    for (int g0 = tb0; g0 < tb1; g0 += 8) {
+        u32x4 raw[8][2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int tj = min(g0 + j, tb1 - 1);      // past the range: a repeat, not stored
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                raw[j][h] = __builtin_nontemporal_load(
+                    (const u32x4*)(w2e + (size_t)(16 * tj + 8 * h + (lane >> 3)) * a.F));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 8 * h + (lane >> 3);
+                *(u32x4*)(wl + j * 2048 + r * 128 + 16 * ((lane & 7) ^ (r & 7))) = raw[j][h];
+            }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const i32x8 w = wl_operand(wl + j * 2048, r16, c1);
+            const bool live = g0 + j < tb1;
 #pragma unroll
             for (int t = 0; t < NTB; ++t) {
-                xb[t] = read_op(slot + kWBytes, 16 * t + l16, c1);
-                sx[t] = s_xs[(16 * t + l16) * kXsStride + k];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const i32x8 w = read_op(slot, (j < 2 ? 32 * wave + 16 * j : 128 + 32 * wave + 16 * (j - 2)) + l16, c1);
-                const float ws = j < 2 ? wg : wu;
-#pragma unroll
-                for (int t = 0; t < NTB; ++t) {
-                    const f32x4 p = mfma_fp8(w, xb[t]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j][t][i] = fmaf(p[i], ws * sx[t], acc[j][t][i]);
-                }
-            }
-            if (k == nkb - 1) {
-                // SwiGLU of the slice; lane: token 16t + l16, features 32w + 16jj + 4*c1 + i
-                float act[2][NTB][4];
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                    for (int t = 0; t < NTB; ++t)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) act[jj][t][i] = swiglu(acc[jj][t][i], acc[jj + 2][t][i]);
-                // one 1x128 block per token: amax over lanes, then over wavefronts
-#pragma unroll
-                for (int t = 0; t < NTB; ++t) {
-                    float m = 0.f;
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(act[jj][t][i]));
-                    m = fmaxf(m, __shfl_xor(m, 16));
-                    m = fmaxf(m, __shfl_xor(m, 32));
-                    if (c1 == 0) s_amax[wave * 16 * kTBMax + 16 * t + l16] = m;
-                }
-                lds_barrier();
-#pragma unroll
-                for (int t = 0; t < NTB; ++t) {
-                    const int tok = 16 * t + l16;
-                    float m = s_amax[tok];
-#pragma unroll
-                    for (int w = 1; w < 4; ++w) m = fmaxf(m, s_amax[w * 16 * kTBMax + tok]);
-                    const float sc = e4m3_scale(m);
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        const int chunk = 2 * wave + jj;
-                        *(uint32_t*)(s_aq + tok * 128 + 16 * (chunk ^ (tok & 7)) + 4 * c1) =
-                            e4m3_pack4(act[jj][t][0], act[jj][t][1], act[jj][t][2], act[jj][t][3], sc);
-                    }
-                    if (wave == 0 && c1 == 0 && tok < mv) a.asc[(size_t)(crow + tok) * S + s] = sc;
-                }
-                lds_barrier();
-#pragma unroll
-                for (int t = 0; t < NTB; ++t) bq[t] = read_op(s_aq, 16 * t + l16, c1);
-            }
-        } else {
-            // FC2: stage rows 64w + 16jt, raw block products to the partial buffer
-            const int h0 = (k - nkb) * kStRows + 64 * wave;
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const int hb = h0 + 16 * jt;
-                const i32x8 w = read_op(slot, 64 * wave + 16 * jt + l16, c1);
-#pragma unroll
-                for (int t = 0; t < NTB; ++t) {
-                    const f32x4 p = mfma_fp8(w, bq[t]);
-                    const int tok = 16 * t + l16;
-                    if (hb < a.H && tok < mv)
-                        *(f32x4*)(a.part + ((size_t)s * a.TK + crow + tok) * a.H + hb + 4 * c1) = p;
-                }
+                const f32x4 p = mfma_fp8(w, bq[t]);
+                const int tok = 16 * t + r16;
+                if (live && tok < mv)
+                    *(f32x4*)(a.part + ((size_t)s * a.TK + crow + tok) * a.H + 16 * (g0 + j) + 4 * c1) = p;
             }
         }
     }
 }
 
 // Rows of a touched expert: bf16 expert output = sum over slices s (in
-// ascending order) of fma(block product, weight scale x activation scale),
-// eight slices' loads issued together.
-__device__ void reduce_expert(const FusedArgs& a, const float* __restrict__ w2s, int e, long long seg, int me,
-                              int crow0) {
+// ascending order) of fma(block product, weight scale x activation scale).
+// The scales are staged in LDS; each item's partials (up to 16 slices) are
+// loaded together.
+__device__ void reduce_expert(const FusedArgs& a, const float* __restrict__ w2s, unsigned char* smem, int e,
+                              long long seg, int me, int crow0) {
     const int S = a.F / kSlice, nbh = a.H / 128;
     const int n4 = a.H / 4;
-    for (long long q = threadIdx.x; q < (long long)me * n4; q += blockDim.x) {
-        const int i = (int)(q / n4), h = (int)(q - (long long)i * n4) * 4;
-        const float* ws = w2s + ((size_t)e * nbh + h / 128) * S;
-        const float* as = a.asc + (size_t)(crow0 + i) * S;
-        const float* pp = a.part + (size_t)(crow0 + i) * a.H + h;
-        const size_t sstride = (size_t)a.TK * a.H;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < S; s0 += 8) {
-            f32x4 p[8];
-            float sc[8];
+    float* s_ws = (float*)smem;                          // [nbh][S]
+    float* s_as = (float*)(smem + kMaxKB * kMaxKB * 4);  // [64][S]
+    const size_t sstride = (size_t)a.TK * a.H;
+    for (int q = threadIdx.x; q < nbh * S; q += blockDim.x) s_ws[q] = w2s[(size_t)e * nbh * S + q];
+    for (int i0 = 0; i0 < me; i0 += 64) {
+        const int nrow = min(64, me - i0);
+        __syncthreads();
+        for (int q = threadIdx.x; q < nrow * S; q += blockDim.x) s_as[q] = a.asc[(size_t)(crow0 + i0) * S + q];
+        __syncthreads();
+        for (int q = threadIdx.x; q < nrow * n4; q += blockDim.x) {
+            const int i = q / n4, h = (q - i * n4) * 4;
+            const float* pp = a.part + (size_t)(crow0 + i0 + i) * a.H + h;
+            const float* ws = s_ws + (h / 128) * S;
+            const float* as = s_as + i * S;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < S; s0 += 16) {
+                f32x4 p[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {   // past S: an in-bounds slice, not accumulated
-                const int su = min(s0 + u, S - 1);
-                p[u] = *(const f32x4*)(pp + (size_t)su * sstride);
-                sc[u] = ws[su] * as[su];
-            }
+                for (int u = 0; u < 16; ++u)   // past S: an in-bounds slice, not accumulated
+                    p[u] = *(const f32x4*)(pp + (size_t)min(s0 + u, S - 1) * sstride);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (s0 + u < S) {
+                for (int u = 0; u < 16; ++u) {
+                    if (s0 + u < S) {
+                        const float sc = ws[s0 + u] * as[s0 + u];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] = fmaf(p[u][r], sc[u], acc[r]);
+                        for (int r = 0; r < 4; ++r) acc[r] = fmaf(p[u][r], sc, acc[r]);
+                    }
                 }
             }
+            u32x2 o;
+            o[0] = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+            o[1] = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+            *(u32x2*)(a.eo + (size_t)(seg + i0 + i) * a.H + h) = o;
         }
-        u32x2 o;
-        o[0] = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-        o[1] = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-        *(u32x2*)(a.eo + (size_t)(seg + i) * a.H + h) = o;
     }
 }
 
-// The routing arrays and W2 scales come in again as restrict parameters: the
-// kernel never writes them, so uniform reads of them can use scalar loads.
-__global__ __launch_bounds__(256, 1) void k_decode_fused(FusedArgs a, const int32_t* __restrict__ row_id,
-                                                         const float* __restrict__ copy_prob,
-                                                         const int32_t* __restrict__ src_row,
-                                                         const int32_t* __restrict__ act_list,
-                                                         const int32_t* __restrict__ coff,
-                                                         const float* __restrict__ w2s) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes + 4 * 16 * kTBMax * 4];
+// The routing arrays and weight scales come in again as restrict parameters:
+// the kernel never writes them, so uniform reads of them can use scalar loads.
+__global__ __launch_bounds__(kWaves * 64, 2) void k_decode_fused(FusedArgs a, const int32_t* __restrict__ row_id,
+                                                                 const float* __restrict__ copy_prob,
+                                                                 const int32_t* __restrict__ src_row,
+                                                                 const int32_t* __restrict__ act_list,
+                                                                 const int32_t* __restrict__ coff,
+                                                                 const float* __restrict__ w1s,
+                                                                 const float* __restrict__ w2s) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
     __shared__ int s_last, s_ntok;
     __shared__ int s_tok[64];
     const int lane = threadIdx.x & 63;
@@ -424,36 +333,46 @@ __global__ __launch_bounds__(256, 1) void k_decode_fused(FusedArgs a, const int3
         const int crow0 = coff[ai];
         for (int m0 = 0; m0 < me; m0 += 16 * kTBMax) {
             const int mv = min(16 * kTBMax, me - m0);
-            if (mv <= 16) fused_pass<1>(a, smem, e, s, seg, m0, mv, crow0 + m0, lane, wave);
-            else fused_pass<2>(a, smem, e, s, seg, m0, mv, crow0 + m0, lane, wave);
+            if (mv <= 16) fused_pass<1>(a, w1s, smem, e, s, seg, m0, mv, crow0 + m0, lane, wave);
+            else fused_pass<2>(a, w1s, smem, e, s, seg, m0, mv, crow0 + m0, lane, wave);
         }
-        // publish this slice; the last of the expert's S slices reduces it
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // publish this slice: every wavefront's stores are complete at the
+        // barrier, then one release increment (it writes back this XCD's L2);
+        // the last of the expert's S slices acquires and reduces the expert
+        wait_stores();
         __syncthreads();
-        if (threadIdx.x == 0)
-            s_last = __hip_atomic_fetch_add(a.cnt_e + ai, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+        if (threadIdx.x == 0) {
+            const int last =
+                __hip_atomic_fetch_add(a.cnt_e + ai, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_last = last;
+        }
         __syncthreads();
         if (!s_last) continue;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        reduce_expert(a, w2s, e, seg, me, crow0);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        reduce_expert(a, w2s, smem, e, seg, me, crow0);
         // publish the expert rows; a token whose copies are all reduced is combined here
         for (int i0 = 0; i0 < me; i0 += 64) {
+            wait_stores();
             __syncthreads();
             if (threadIdx.x == 0) s_ntok = 0;
             __syncthreads();
-            if (wave == 0 && i0 + lane < me) {
-                const int t = src_row[seg + i0 + lane];
-                const int nv = count_copies(row_id, a.K, a.R, t);
-                if (__hip_atomic_fetch_add(a.cnt_t + t, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == nv - 1)
-                    s_tok[atomicAdd(&s_ntok, 1)] = t;
+            if (wave == 0) {
+                bool done = false;
+                int t = 0;
+                if (i0 + lane < me) {
+                    t = src_row[seg + i0 + lane];
+                    const int nv = count_copies(row_id, a.K, a.R, t);
+                    done = __hip_atomic_fetch_add(a.cnt_t + t, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) ==
+                           nv - 1;
+                }
+                if (__ballot(done) != 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                if (done) s_tok[atomicAdd(&s_ntok, 1)] = t;
             }
             __syncthreads();
             const int ntok = s_ntok;
-            if (ntok > 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            for (int q = 0; q < ntok; ++q)
-                combine_token_wg((const u32x4*)a.eo, a.K, a.H / 8, (int)a.R, row_id, copy_prob, a.apply,
-                                 (u32x4*)a.y, s_tok[q], wave, lane);
+            for (int q = wave; q < ntok; q += kWaves)
+                combine_token_wave((const u32x4*)a.eo, a.K, a.H / 8, (int)a.R, row_id, copy_prob, a.apply,
+                                   (u32x4*)a.y, s_tok[q], lane);
         }
         __syncthreads();
     }
@@ -488,7 +407,9 @@ size_t decode_fused_scratch_bytes(long long R, int T, int K, int H, int F, int E
     return fused_layout(R, T, K, H, F, E).total;
 }
 
-bool decode_fused_shape_ok(int H, int F) { return H % 128 == 0 && H / 128 <= kMaxKB && F % kSlice == 0; }
+bool decode_fused_shape_ok(int H, int F) {
+    return H % 128 == 0 && H / 128 <= kMaxKB && F % kSlice == 0 && F / kSlice <= kMaxKB;
+}
 
 hipError_t launch_decode_fused(const moe_handle* h, int F, const void* x, const void* w1, const float* w1s,
                                const void* w2, const float* w2s, void* scratch, void* expert_out, int apply_probs,
@@ -529,8 +450,8 @@ hipError_t launch_decode_fused(const moe_handle* h, int F, const void* x, const 
     a.TK = d.T * d.K;
     a.apply = apply_probs;
     hipLaunchKernelGGL(k_fused_prep, dim3(d.T + 1), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_decode_fused, dim3(num_cu), dim3(256), 0, s, a, a.row_id, a.copy_prob, a.src_row,
-                       (const int32_t*)a.act_list, (const int32_t*)a.coff, a.w2s);
+    hipLaunchKernelGGL(k_decode_fused, dim3(2 * num_cu), dim3(kWaves * 64), 0, s, a, a.row_id, a.copy_prob, a.src_row,
+                       (const int32_t*)a.act_list, (const int32_t*)a.coff, a.w1s, a.w2s);
     return hipGetLastError();
 }
 

@@ -133,23 +133,24 @@ __device__ __forceinline__ i32x8 wl_operand(const unsigned char* tile, int r, in
 
 constexpr int kWaveLds = kU * 4096;   // bytes of a wavefront's weight buffer
 
-// One pass over up to 16*NTB rows (m0 .. m0+mv-1 of the segment) for this
-// wavefront's two 16-row weight tiles (FC1: gate and up rows of 16 features;
-// FC2: 32 consecutive output rows); NTB token blocks of 16 rows.  t0 / t1
-// point at byte 0 of the first row of each tile; lds is this wavefront's
-// kWaveLds-byte buffer.  Per group of kU K blocks the weights are loaded as
-// whole lines, passed through the buffer into operand layout, then
-// multiplied with the token codes (loaded per K block from the quantised
-// rows).
-template <int MODE, int NTB>
-__device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const float* __restrict__ Xs,
-                                         const uint8_t* t0, const uint8_t* t1, const float* sg, const float* su,
-                                         void* __restrict__ Outv, long long seg, int m0, int mv, int Kdim, int Nout,
-                                         int f0, int lane, unsigned char* lds) {
+// K loop of one pass over up to 16*NTB rows (m0 .. m0+mv-1 of the segment)
+// for this wavefront's two 16-row weight tiles (FC1: gate and up rows of 16
+// features; FC2: 32 consecutive output rows); NTB token blocks of 16 rows.
+// t0 / t1 point at byte 0 of the first row of each tile; sg / su are the
+// tiles' weight scales per K block; lds is this wavefront's kWaveLds-byte
+// buffer.  Per group of kU K blocks the weights are loaded as whole lines,
+// passed through the buffer into operand layout, then multiplied with the
+// token codes (loaded per K block from the quantised rows).  On return lane
+// l holds, for token m0 + 16t + l%16, the fp32 sums of tile rows 4*(l/16)+i
+// in acc_g[t][i] / acc_u[t][i].
+template <int NTB>
+__device__ __forceinline__ void fp8_accumulate(const uint8_t* __restrict__ Xq, const float* __restrict__ Xs,
+                                               const uint8_t* t0, const uint8_t* t1, const float* sg,
+                                               const float* su, long long seg, int m0, int mv, int Kdim, int lane,
+                                               unsigned char* lds, f32x4 (&acc_g)[NTB], f32x4 (&acc_u)[NTB]) {
     constexpr int U = kU;
     const int kq = (lane >> 4) * 16, c1 = lane >> 4, r16 = lane & 15;
     const int nkb = Kdim / 128;
-    f32x4 acc_g[NTB], acc_u[NTB];
 #pragma unroll
     for (int t = 0; t < NTB; ++t) {
         acc_g[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -194,6 +195,18 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
     for (; kb + U <= nkb; kb += U) group(kb, std::integral_constant<int, U>{});
     for (; kb < nkb; ++kb) group(kb, std::integral_constant<int, 1>{});
 
+}
+
+// One pass of a work unit: the K loop, then the epilogue.
+// MODE 0: SwiGLU of (gate, up) stored as fp32 [rows, Nout] at features
+// f0 + 4*(lane/16) + i; MODE 1: both tiles stored as bf16 at output rows f0..
+template <int MODE, int NTB>
+__device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const float* __restrict__ Xs,
+                                         const uint8_t* t0, const uint8_t* t1, const float* sg, const float* su,
+                                         void* __restrict__ Outv, long long seg, int m0, int mv, int Kdim, int Nout,
+                                         int f0, int lane, unsigned char* lds) {
+    f32x4 acc_g[NTB], acc_u[NTB];
+    fp8_accumulate<NTB>(Xq, Xs, t0, t1, sg, su, seg, m0, mv, Kdim, lane, lds, acc_g, acc_u);
     // ---- epilogue: lane holds token m0+16t+lane%16, features f0+4*(lane/16)+i
 #pragma unroll
     for (int t = 0; t < NTB; ++t) {
@@ -385,6 +398,15 @@ __device__ __forceinline__ void combine_token_wg(const u32x4* __restrict__ Y, in
             }
         }
     }
+}
+
+// Combine of token t by one wavefront: the four quarters of the workgroup
+// form above, one after the other (same arithmetic, same result).
+__device__ __forceinline__ void combine_token_wave(const u32x4* __restrict__ Y, int K, int nch, int R,
+                                                   const int32_t* __restrict__ row_id,
+                                                   const float* __restrict__ copy_prob, int apply,
+                                                   u32x4* __restrict__ y, int t, int lane) {
+    for (int w = 0; w < 4; ++w) combine_token_wg(Y, K, nch, R, row_id, copy_prob, apply, y, t, w, lane);
 }
 
 }  // namespace ops
