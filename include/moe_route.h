@@ -132,7 +132,9 @@ const char* moe_status_string(int status);
 
 /* Largest number of rows the padded segments can need:
  * min(E * roundup(capacity, p), T*K + E*(p-1)); the second term alone when
- * capacity < 0.  Returns -1 for an invalid descriptor. */
+ * capacity < 0.  This is the static output bound of [P3] "What does this PR
+ * do ?" (the permuted buffer sized from host-known numbers so that no device
+ * count is read back).  Returns -1 for an invalid descriptor. */
 int64_t moe_out_rows_bound(const moe_desc* desc);
 
 /* Bytes of one routing tensor of this descriptor: T*E for the Boolean map,
@@ -145,7 +147,11 @@ int64_t moe_routing_bytes(const moe_desc* desc);
  * factor <= 0. */
 int64_t moe_capacity_from_rows(int64_t rows, double factor);
 
-/* Workspace bytes needed by a handle for this descriptor (0 if invalid). */
+/* Workspace bytes needed by a handle for this descriptor (0 if invalid): the
+ * routing metadata of moe_handle (per-tile masks and bases, per-expert counts
+ * and offsets, the row map), sized from the descriptor alone, so the caller
+ * can own and reuse it ([P1] "Summary": caller-owned buffers reused across
+ * steps; [P2] "Summary": a routing buffer reused instead of reallocated). */
 size_t moe_workspace_bytes(const moe_desc* desc);
 
 /* Validate `desc`, resolve out_rows, carve the caller's workspace d_ws
@@ -208,7 +214,9 @@ int moe_dispatch(moe_handle* h, const void* d_routing, const float* d_probs,
                  int32_t* d_flag, void* stream);
 
 /* Scratch bytes moe_grouped_swiglu_mlp needs for FFN width F and weight
- * dtype wdtype: MOE_BF16 holds the bf16 FC1 activations of all R rows;
+ * dtype wdtype (the FC1 -> activation -> FC2 intermediate of [P1]
+ * "Configuration", owned by the caller): MOE_BF16 holds the bf16 FC1
+ * activations of all R rows;
  * MOE_FP8E4M3_B128 holds the fp32 FC1 activations plus the e4m3 codes and
  * fp32 1x128 scales of the permuted rows and of the activations (each input
  * is quantised once per call).  0 if invalid. */
