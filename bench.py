@@ -70,7 +70,7 @@ def cpu_model() -> str:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=256, help="oracle MLP sample size (0 = no CPU baseline)")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
