@@ -375,8 +375,6 @@ int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const
     return moe_grouped_fc2(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, d_expert_out, stream);
 }
 
-constexpr int kDecodeLayerEnabled = 0;
-
 size_t moe_decode_layer_scratch_bytes(const moe_handle* h, int32_t F) {
     if (!h || F <= 0 || F % 128 || h->desc.H % 128) return 0;
     return up(decode_layer_scratch_bytes((long long)h->desc.out_rows, h->desc.H, F), kAlign);
@@ -397,10 +395,6 @@ int moe_decode_layer_fp8(const moe_handle* h, int32_t F, const void* d_x, const 
         return MOE_EALIGN;
     if ((d_x && !al16(d_x)) || (d_expert_out && !al16(d_expert_out)) || (d_y && !al16(d_y))) return MOE_EALIGN;
     if (scratch_bytes < moe_decode_layer_scratch_bytes(h, F)) return MOE_ENOSPC;
-    // Switched off: the first MI355X run of this kernel (16 tokens) did not
-    // finish within minutes, and no mistake in the kernel has been shown that
-    // explains it; nothing is launched until one is.
-    if (kDecodeLayerEnabled == 0) return MOE_EUNSUPPORTED;
     const int ncu = num_cu();
     if (ncu <= 0) return MOE_EHIP;
     return hip_rc(launch_decode_layer(h, F, d_x, d_w1, d_w1_scales, d_w2, d_w2_scales, d_scratch, d_expert_out,

@@ -19,23 +19,38 @@
 //   Q(a)     quantise that expert's activation rows                 needs its F1
 //   F2(a,u)  FC2 unit u of the expert                               needs its Q
 //   C(t)     combine of token t                                     needs all F2
-// Items are spread over 8 queues (tokens t % 8, experts a % 8); each queue
-// lists its items in the global order and hands them out by an atomic ticket.
-// Workgroup b takes tickets from queue b % 8.  A workgroup only ever waits on
-// items of lower global order.  The lowest unfinished item is therefore
-// always claimable: everything its queue's workgroups hold is lower, hence
-// finished, so they take it next; its owner is running (a ticket is taken by
-// a running workgroup) and its own dependencies are finished.  Progress does
-// not depend on how many workgroups are resident at once.
+// Items are spread over 8 queues, one per XCD (tokens t % 8, experts a % 8);
+// a workgroup takes tickets from the queue of the XCD it runs on (hardware
+// register XCC_ID), so every F1 -> Q -> F2 dependency stays inside one XCD
+// and its L2.  A workgroup only ever waits on items of lower global order.
+// The lowest unfinished item is therefore always claimable: everything its
+// queue's workgroups hold is lower, hence finished, so they take it next;
+// its owner is running (a ticket is taken by a running workgroup) and its own
+// dependencies are finished.  Progress does not depend on how many
+// workgroups are resident at once, only on every XCD running at least one.
 //
-// Completion is published with a release atomic add at agent scope after a
-// workgroup barrier (the producer's stores are written back from its XCD's
-// L2); a waiter polls the counter with agent-scope relaxed loads (coherent
-// across XCDs), then every thread takes an agent-scope acquire fence before
-// reading the produced data.  Every wait is bounded by the 100 MHz real-time
-// counter: past the bound it sets bit 0 of the caller's status word and
-// proceeds, and once the status is set later waits return at once, so the
-// kernel always runs to its end.
+// Visibility.  Each XCD has its own L2; an acquire or release at agent scope
+// invalidates or writes back the whole L2 of the XCD, which made the first
+// form of this kernel (every dependency at agent scope) 1.7x slower.  Here a
+// finished item's stores have completed in its XCD's L2 before the barrier
+// that ends it (s_waitcnt vmcnt(0) in every wavefront).  Then:
+//   * F1 and Q items (read only on their own XCD) are counted with relaxed
+//     increments, and their readers, after seeing the count, invalidate only
+//     the CU's L1 (buffer_inv sc0): the data are in the shared L2;
+//   * D items (token rows read on every XCD) are counted with release
+//     increments at agent scope (L2 written back); each workgroup takes one
+//     acquire at agent scope (L2 and L1 invalidated) before its first F1
+//     item, after the count shows every D item done;
+//   * F2 items are counted per queue with relaxed increments; the increment
+//     that completes a queue writes back the XCD's L2 (release at agent scope,
+//     covering every F2 item of the queue) and counts the queue; C items wait
+//     for every queue, then acquire at agent scope.
+// Counters are polled with agent-scope relaxed loads.  Every wait is bounded
+// by the 100 MHz real-time counter: past the bound it sets bit 0 of the
+// caller's status word and proceeds, and once the status is set later waits
+// return at once, so the kernel always runs to its end.  A workgroup whose
+// XCC_ID is 8 or more sets bit 1 and does nothing (the queues assume eight
+// XCDs numbered 0-7).
 #include "device_ops.h"
 
 namespace moe {
@@ -43,13 +58,16 @@ namespace {
 
 using namespace ops;
 
-constexpr int kQueues = 8;
+constexpr int kQueues = 8;                            // one per XCD
 constexpr int kCtlStride = 32;                        // ints between shared counters (128 bytes)
 constexpr int kCtlDispatch = kQueues * kCtlStride;    // D items done
-constexpr int kCtlFc2 = kCtlDispatch + kCtlStride;    // F2 items done (all experts)
+constexpr int kCtlFc2 = kCtlDispatch + kCtlStride;    // queues whose F2 items are all done
 constexpr int kCtlFc1 = kCtlFc2 + kCtlStride;         // F1 items done, per active expert
 constexpr int kCtlQuant = kCtlFc1 + kMaxE;            // Q item done, per active expert
-constexpr int kCtlInts = kCtlQuant + kMaxE;
+constexpr int kCtlFc2Q = kCtlQuant + kMaxE;           // F2 items done, per queue
+constexpr int kCtlInts = kCtlFc2Q + kQueues * kCtlStride;
+// how a finished item is published (see the claim loop)
+constexpr int kPubRelease = 1, kPubLocal = 2, kPubFc2 = 3;
 constexpr long long kWaitTicks = 25000000;            // 0.25 s of the 100 MHz real-time counter
 
 struct DecodeArgs {
@@ -80,9 +98,12 @@ __global__ __launch_bounds__(256) void k_decode_reset(int* __restrict__ ctl, int
     if (threadIdx.x == 0) status[0] = 0;
 }
 
-// Thread 0: wait until *c >= target (bounded); then every thread acquires.
-__device__ __forceinline__ void wait_count(const DecodeArgs& a, int* c, int target) {
-    if (threadIdx.x == 0) {
+// Thread 0: wait until *c >= target (bounded).  (The branch is taken per
+// wavefront, then per lane inside wavefront 0.)  The caller then acquires:
+// acquire_agent for data written on another XCD, acquire_local for data
+// written on this one.
+__device__ __forceinline__ void wait_count(const DecodeArgs& a, int* c, int target, int wave, int lane) {
+    if (wave == 0 && lane == 0) {
         if (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
             const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
             while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -95,15 +116,40 @@ __device__ __forceinline__ void wait_count(const DecodeArgs& a, int* c, int targ
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// Publish one finished item: every thread's stores are done at the barrier,
-// then thread 0 releases them at agent scope with the counter increment.
-__device__ __forceinline__ void signal_done(int* c) {
+// Data written on any XCD: invalidate this CU's L1 and this XCD's L2.
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Data written by a workgroup on this XCD: it sits in this XCD's L2 (the
+// producer's stores completed there before its counter increment), so only
+// this CU's L1 can hold an older copy; invalidate the L1 alone.
+__device__ __forceinline__ void acquire_local() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
+// End of an item: this wavefront's stores have completed, then the barrier.
+__device__ __forceinline__ void finish_item() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Publishing a finished item: every thread's stores have completed in this
+// XCD's L2 at the barrier that ends the item (finish_item); at the top of the
+// next turn of the claim loop, lane 0 of wavefront 0 increments the item's
+// counter, then claims the next ticket.  D items are read on every XCD: their
+// increment is a release at agent scope (this XCD's L2 is written back first).
+// F1 and Q items are read only on their own XCD: a relaxed increment (no
+// write-back).  F2 items count per queue; the increment that completes a
+// queue writes back this XCD's L2 (every F2 item of the queue has completed
+// its stores in it) and counts the queue done, with a release at agent scope;
+// C items wait for every queue.
+//
+// The claim loop keeps its control flow uniform across each wavefront: the
+// claim is made inside a branch on the wavefront index and read back from
+// LDS with readfirstlane.  A thread-0-only increment at the end of an item
+// followed by a thread-0-only claim at the loop top lets the compiler send
+// the other lanes of wavefront 0 (and every lane of the other wavefronts)
+// straight back to the loop's barrier, where they re-read the old ticket and
+// repeat the same item without end; no such pair is left in the loop.
 
 __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
     __shared__ int s_list[kMaxE];    // experts holding rows, ascending
@@ -112,7 +158,13 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
     __shared__ int s_ticket;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q = blockIdx.x % kQueues;
+    // The queue is this workgroup's XCD (hardware register XCC_ID), so the
+    // producer and consumer of every F1 -> Q -> F2 dependency share an L2.
+    const int q = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg(20 | (15 << 11)));   // XCC_ID[15:0]
+    if (q >= kQueues) {
+        if (tid == 0) __hip_atomic_fetch_or(a.status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
 
     // ---- experts holding rows (every workgroup builds the same list) ----------
     if (wave == 0) {
@@ -143,11 +195,30 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
     const int nbF = a.F / 128, ngF = (nbF + kQBlocks - 1) / kQBlocks;
     int* ctl = a.ctl;
 
+    const int nF2q = eF2 - eQ;           // F2 items of this queue
+    int* done = nullptr;                 // counter of the item finished last turn
+    int pub = 0;                         // and how it is published
+    bool have_d = false;                 // this workgroup has acquired the D items' rows
     for (;;) {
-        if (tid == 0) s_ticket = __hip_atomic_fetch_add(ctl + q * kCtlStride, 1, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
+        if (wave == 0) {
+            int tk = 0;
+            if (lane == 0) {
+                if (pub == kPubRelease) {
+                    __hip_atomic_fetch_add(done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                } else if (pub == kPubLocal) {
+                    __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else if (pub == kPubFc2) {
+                    if (__hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nF2q - 1)
+                        __hip_atomic_fetch_add(ctl + kCtlFc2, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                tk = __hip_atomic_fetch_add(ctl + q * kCtlStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            s_ticket = __builtin_amdgcn_readfirstlane(tk);
+        }
+        done = nullptr;
+        pub = 0;
         __syncthreads();
-        const int i = s_ticket;
+        const int i = __builtin_amdgcn_readfirstlane(s_ticket);
         __syncthreads();                 // s_ticket is rewritten by the next claim
         if (i >= eC) break;
         if (i < nD) {
@@ -155,33 +226,48 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
             const long long t = q + (long long)kQueues * i;
             for (int g = wave; g < ngH; g += 4)
                 permute_quant_wave(a.x, a.H, a.K, (int)a.R, a.row_id, a.xq, a.xs, t, g * kPQBlocks, lane);
-            signal_done(ctl + kCtlDispatch);
+            finish_item();
+            done = ctl + kCtlDispatch;
+            pub = kPubRelease;
         } else if (i < eF1) {
             const int k = i - nD, ai = q + kQueues * (k / upe1), u = k % upe1;
-            wait_count(a, ctl + kCtlDispatch, a.T);
+            if (!__builtin_amdgcn_readfirstlane(have_d)) {   // token rows never change after the D items: acquire once
+                wait_count(a, ctl + kCtlDispatch, a.T, wave, lane);
+                acquire_agent();
+                have_d = true;
+            }
             fp8_unit<0>(a.xq, a.xs, a.w1, a.w1s, a.act, a.seg_off, a.kept, a.R, a.H, 2 * a.F, a.F, s_list[ai], u,
                         lane, wave, s_w + wave * kWaveLds);
-            signal_done(ctl + kCtlFc1 + ai);
+            finish_item();
+            done = ctl + kCtlFc1 + ai;
+            pub = kPubLocal;
         } else if (i < eQ) {
             // Q(a): the expert's activation rows, (row, 8-block group) per wavefront
             const int ai = q + kQueues * (i - eF1), e = s_list[ai];
-            wait_count(a, ctl + kCtlFc1 + ai, upe1);
+            wait_count(a, ctl + kCtlFc1 + ai, upe1, wave, lane);
+            acquire_local();
             const long long seg = a.seg_off[e];
             long long me = a.kept[e];
             if (seg + me > a.R) me = a.R - seg;
             for (long long w = wave; w < me * ngF; w += 4)
                 quant_row_wave<float>(a.act, a.F, a.aq, a.as, seg + w / ngF, (int)(w % ngF) * kQBlocks, lane);
-            signal_done(ctl + kCtlQuant + ai);
+            finish_item();
+            done = ctl + kCtlQuant + ai;
+            pub = kPubLocal;
         } else if (i < eF2) {
             const int k = i - eQ, ai = q + kQueues * (k / upe2), u = k % upe2;
-            wait_count(a, ctl + kCtlQuant + ai, 1);
+            wait_count(a, ctl + kCtlQuant + ai, 1, wave, lane);
+            acquire_local();
             fp8_unit<1>(a.aq, a.as, a.w2, a.w2s, a.eo, a.seg_off, a.kept, a.R, a.F, a.H, a.H, s_list[ai], u, lane,
                         wave, s_w + wave * kWaveLds);
-            signal_done(ctl + kCtlFc2);
+            finish_item();
+            done = ctl + kCtlFc2Q + q * kCtlStride;
+            pub = kPubFc2;
         } else {
             // C(t): combine of token t once every FC2 unit is done
             const int t = q + kQueues * (i - eF2);
-            wait_count(a, ctl + kCtlFc2, n_act * upe2);
+            wait_count(a, ctl + kCtlFc2, min(n_act, kQueues), wave, lane);
+            acquire_agent();
             combine_token_wg((const u32x4*)a.eo, a.K, a.H / 8, (int)a.R, a.row_id, a.copy_prob, a.apply,
                              (u32x4*)a.y, t, wave, lane);
             __syncthreads();

@@ -338,11 +338,10 @@ int moe_combine_fp8(const moe_handle* h, const void* d_expert_out_q, const float
  *                  copy are unspecified
  *   d_y            [T,H] bf16 out
  *   d_status       [1] int32 out, written fresh: 0, or bit 0 set if a wait of
- *                  the kernel ran past its bound (0.25 s) and the outputs are
- *                  then unspecified; the kernel always runs to its end.
- * Currently switched off: after all argument checks it returns
- * MOE_EUNSUPPORTED and enqueues nothing (its first run on an MI355X did not
- * finish, with no cause shown yet). */
+ *                  the kernel ran past its bound (0.25 s), bit 1 set if a
+ *                  workgroup ran on an XCD numbered 8 or more (the work queues
+ *                  assume XCDs 0-7); the outputs are then unspecified.  The
+ *                  kernel always runs to its end. */
 size_t moe_decode_layer_scratch_bytes(const moe_handle* h, int32_t F);
 int moe_decode_layer_fp8(const moe_handle* h, int32_t F, const void* d_x, const void* d_w1, const float* d_w1_scales,
                          const void* d_w2, const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,

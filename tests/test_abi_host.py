@@ -391,7 +391,6 @@ def test_decode_layer_argument_checks_before_launch():
     assert call(w2=C.c_void_p(base + 8)) == A.MOE_EALIGN
     assert call(st=C.c_void_p(base + 2)) == A.MOE_EALIGN
     assert call(nbytes=need - 1) == A.MOE_ENOSPC
-    assert call() == A.MOE_EUNSUPPORTED               # switched off: nothing is launched
     d8 = _desc(T=16, H=256, E=8, K=2, payload="fp8")
     rc, h8, base8, n8, _buf8 = _host_handle(d8)
     h8.state = 1

@@ -140,11 +140,6 @@ def test_decode_graph_replay_matches_eager(fp8_weights):
             assert int(d.flag.item()) == 0
 
 
-MEGA_OFF = pytest.mark.skip(reason="persistent decode layer switched off: its first MI355X run (16 tokens) did not "
-                                  "finish within minutes and no cause has been shown; moe_decode_layer_fp8 returns "
-                                  "MOE_EUNSUPPORTED")
-
-
 def _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, scratch=None):
     """preprocess + the persistent decode layer; returns (y, expert_out, status)."""
     scratch = scratch if scratch is not None else torch.empty(d.decode_layer_scratch_bytes(c.F), dtype=torch.uint8,
@@ -157,7 +152,6 @@ def _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, scratch=None):
     return y, eo, st
 
 
-@MEGA_OFF
 @pytest.mark.parametrize("T", [16, 64, 100, 256])
 def test_decode_megakernel_matches_separate_launches_and_oracle(fp8_weights, T):
     """The persistent decode layer (quantise-on-dispatch, FC1, activation
@@ -182,7 +176,6 @@ def test_decode_megakernel_matches_separate_launches_and_oracle(fp8_weights, T):
         assert torch.count_nonzero(y[T:].float()).item() == 0
 
 
-@MEGA_OFF
 def test_decode_megakernel_graph_replay_and_empty_batch(fp8_weights):
     """preprocess + the persistent decode layer captured once per bucket and
     replayed with new inputs (live counts bucket, half, 1 and 0): every replay
@@ -229,7 +222,6 @@ def test_decode_megakernel_graph_replay_and_empty_batch(fp8_weights):
                 assert torch.count_nonzero(yb.float()).item() == 0
 
 
-@MEGA_OFF
 @pytest.mark.parametrize("T,H,E,K,F,pad", [(33, 256, 8, 2, 256, 16), (1, 128, 4, 1, 128, 1), (70, 384, 5, 3, 128, 8)])
 def test_decode_megakernel_small_shapes(T, H, E, K, F, pad):
     """Small shapes, ragged expert counts: bit-identical to the separate
