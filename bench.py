@@ -84,8 +84,9 @@ def main() -> int:
     ap.add_argument("--workload", choices=("dsv3_layer", "decode"), default="dsv3_layer",
                     help="decode: only the fp8 decode layer, eager, for kernel profiling")
     ap.add_argument("--tokens", type=int, default=16, help="decode workload: live tokens (bucket = next pow2)")
-    ap.add_argument("--decode-path", choices=("separate", "fused"), default="separate",
-                    help="decode workload: separate launches or the fused decode layer")
+    ap.add_argument("--decode-path", choices=("separate", "fused", "persistent"), default="separate",
+                    help="decode workload: separate launches, the fused decode layer (two launches) or the "
+                         "persistent decode kernel (one launch)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -517,12 +518,19 @@ def run_decode(args):
     eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
     y = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
 
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
     if args.decode_path == "fused":
         scr = torch.empty(d.decode_fused_scratch_bytes(c.F), dtype=torch.uint8, device=dev)
 
         def step():
             d.preprocess(rt, pt, tl)
             d.decode_fused_fp8(x, w1q, w2q, w1s, w2s, scratch=scr, expert_out=eo, out=y)
+    elif args.decode_path == "persistent":
+        scr = torch.empty(d.decode_layer_scratch_bytes(c.F), dtype=torch.uint8, device=dev)
+
+        def step():
+            d.preprocess(rt, pt, tl)
+            d.decode_layer_fp8(x, w1q, w2q, w1s, w2s, scratch=scr, expert_out=eo, out=y, status=status)
     else:
         def step():
             d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, scratch=scr, expert_out=eo,
@@ -537,11 +545,12 @@ def run_decode(args):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    st = int(status.item())
     print(json.dumps({"workload": f"decode_fp8: {T_live} live tokens (bucket {T}) x {c.H}, {c.E} experts top-{c.K}, "
                                   f"FFN {c.F}, fp8 e4m3 weights", "path": args.decode_path,
-                      "ms_per_layer_eager": round(ms, 4),
+                      "ms_per_layer_eager": round(ms, 4), "status": st,
                       "steps": args.steps}), flush=True)
-    return 0
+    return 0 if st == 0 else 1
 
 
 def run_workloads():
@@ -690,6 +699,21 @@ def run_workloads():
         fm, fmed = _graph_times(fstep)
         torch.cuda.synchronize()
         same = bool(torch.equal(fy.view(torch.int16), y.view(torch.int16)))
+        # the persistent decode kernel: preprocess + one launch (dispatch, FC1, FC2, combine)
+        dp = Dispatcher(T, c.H, c.E, c.K, pad_multiple=c.pad)
+        pscr = torch.empty(dp.decode_layer_scratch_bytes(c.F), dtype=torch.uint8, device=dev)
+        peo = torch.empty((dp.R, c.H), dtype=torch.bfloat16, device=dev)
+        py = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
+        pst = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+        def pstep():
+            dp.preprocess(rt, pt)
+            dp.decode_layer_fp8(x, w1q, w2q, w1s, w2s, scratch=pscr, expert_out=peo, out=py, status=pst)
+
+        pm, pmed = _graph_times(pstep)
+        torch.cuda.synchronize()
+        psame = bool(torch.equal(py.view(torch.int16), y.view(torch.int16)))
+        pstatus = int(pst.item())
         out5[f"T{T}"] = {"graph_min_ms": round(gm, 4), "graph_median_ms": round(gmed, 4),
                          "tokens_per_s": round(T / (gm * 1e-3), 1), "experts_touched": touched,
                          "weight_bytes": wbytes, "weight_GB_s": round(wbytes / (gm * 1e-3) / 1e9, 1),
@@ -698,8 +722,13 @@ def run_workloads():
                                    "tokens_per_s": round(T / (fm * 1e-3), 1),
                                    "weight_GB_s": round(wbytes / (fm * 1e-3) / 1e9, 1),
                                    "frac_of_hbm_roofline": round(wbytes / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                   "bit_identical_to_separate": same}}
-        del d, perm, scr, eo, y, df, fscr, feo, fy
+                                   "bit_identical_to_separate": same},
+                         "persistent": {"graph_min_ms": round(pm, 4), "graph_median_ms": round(pmed, 4),
+                                        "tokens_per_s": round(T / (pm * 1e-3), 1),
+                                        "weight_GB_s": round(wbytes / (pm * 1e-3) / 1e9, 1),
+                                        "frac_of_hbm_roofline": round(wbytes / (pm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "bit_identical_to_separate": psame, "status": pstatus}}
+        del d, perm, scr, eo, y, df, fscr, feo, fy, dp, pscr, peo, py, pst
     res["decode_fp8_7168_e256"] = out5
     del w1q, w1s, w2q, w2s
     torch.cuda.empty_cache()

@@ -71,6 +71,7 @@ SIGNATURES = [
     ("moe_ring_release", C.c_int, [C.POINTER(MoeRing), C.c_int32, _P]),
     ("moe_ring_destroy", C.c_int, [C.POINTER(MoeRing)]),
     ("moe_decode_layer_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32]),
+    ("moe_decode_layer_set_wait_bound", None, [C.c_int64]),
     ("moe_decode_layer_fp8", C.c_int, [C.POINTER(MoeHandle), C.c_int32, _P, _P, _P, _P, _P, _P, C.c_size_t, _P,
                                        C.c_int32, _P, _P, _P]),
     ("moe_decode_fused_scratch_bytes", C.c_size_t, [C.POINTER(MoeHandle), C.c_int32]),

@@ -465,8 +465,11 @@ class Dispatcher:
         """The rest of the layer after preprocess(), as one persistent kernel:
         quantise-on-dispatch, FC1 + SwiGLU, activation quantiser, FC2 into
         ``expert_out`` and the combine into ``out``, with fp8 weights.
-        ``status`` (one int32 on the device) is written 0, or 1 if a wait of
-        the kernel ran past its bound."""
+        ``status`` (one int32 on the device): the call clears bits 0 and 1
+        and keeps bit 2, the caller's abort request (every wait returns at
+        once).  Afterwards bit 0 means a wait ran past its bound and bit 1 a
+        workgroup on an XCD numbered 8 or more; with any bit set the outputs
+        are unspecified."""
         _need(self.payload == A.BF16, "the decode layer takes bf16 token rows")
         self._check_x(x)
         F, wdtype = self._check_w1(w1, w1_scales)

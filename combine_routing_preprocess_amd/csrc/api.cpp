@@ -4,6 +4,7 @@
 // device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -375,6 +376,14 @@ int moe_grouped_swiglu_mlp(const moe_handle* h, int32_t F, int32_t wdtype, const
     return moe_grouped_fc2(h, F, wdtype, d_w2, d_w2_scales, d_scratch, scratch_bytes, d_expert_out, stream);
 }
 
+// bound of every wait of the persistent decode kernel (100 MHz ticks)
+constexpr long long kDecodeWaitTicksDefault = 25000000;   // 0.25 s
+static std::atomic<long long> g_decode_wait_ticks{kDecodeWaitTicksDefault};
+
+void moe_decode_layer_set_wait_bound(int64_t ticks) {
+    g_decode_wait_ticks.store(ticks > 0 ? (long long)ticks : kDecodeWaitTicksDefault);
+}
+
 size_t moe_decode_layer_scratch_bytes(const moe_handle* h, int32_t F) {
     if (!h || F <= 0 || F % 128 || h->desc.H % 128) return 0;
     return up(decode_layer_scratch_bytes((long long)h->desc.out_rows, h->desc.H, F), kAlign);
@@ -398,7 +407,8 @@ int moe_decode_layer_fp8(const moe_handle* h, int32_t F, const void* d_x, const 
     const int ncu = num_cu();
     if (ncu <= 0) return MOE_EHIP;
     return hip_rc(launch_decode_layer(h, F, d_x, d_w1, d_w1_scales, d_w2, d_w2_scales, d_scratch, d_expert_out,
-                                      apply_probs ? 1 : 0, d_y, d_status, ncu, (hipStream_t)stream));
+                                      apply_probs ? 1 : 0, d_y, d_status, g_decode_wait_ticks.load(), ncu,
+                                      (hipStream_t)stream));
 }
 
 size_t moe_decode_fused_scratch_bytes(const moe_handle* h, int32_t F) {

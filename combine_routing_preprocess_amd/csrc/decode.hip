@@ -46,11 +46,13 @@
 //     covering every F2 item of the queue) and counts the queue; C items wait
 //     for every queue, then acquire at agent scope.
 // Counters are polled with agent-scope relaxed loads.  Every wait is bounded
-// by the 100 MHz real-time counter: past the bound it sets bit 0 of the
-// caller's status word and proceeds, and once the status is set later waits
-// return at once, so the kernel always runs to its end.  A workgroup whose
-// XCC_ID is 8 or more sets bit 1 and does nothing (the queues assume eight
-// XCDs numbered 0-7).
+// by the 100 MHz real-time counter (0.25 s unless the caller sets another
+// bound): past the bound it sets bit 0 of the caller's status word and
+// proceeds, and once any status bit is set every wait returns at once, so the
+// kernel always runs to its end.  Bit 2 is the caller's abort request: set
+// before the call or while the kernel runs, it ends every wait (the reset
+// keeps it).  A workgroup whose XCC_ID is 8 or more sets bit 1 and does
+// nothing (the queues assume eight XCDs numbered 0-7).
 #include "device_ops.h"
 
 namespace moe {
@@ -68,7 +70,9 @@ constexpr int kCtlFc2Q = kCtlQuant + kMaxE;           // F2 items done, per queu
 constexpr int kCtlInts = kCtlFc2Q + kQueues * kCtlStride;
 // how a finished item is published (see the claim loop)
 constexpr int kPubRelease = 1, kPubLocal = 2, kPubFc2 = 3;
-constexpr long long kWaitTicks = 25000000;            // 0.25 s of the 100 MHz real-time counter
+// status bits: a wait ran past its bound; a workgroup ran on an XCD numbered
+// 8 or more; the caller's abort request (kept by the reset)
+constexpr int kStatusTimeout = 1, kStatusPlacement = 2, kStatusAbort = 4;
 
 struct DecodeArgs {
     const uint16_t* x;          // [T,H] bf16 tokens
@@ -88,14 +92,15 @@ struct DecodeArgs {
     uint16_t* eo;               // [R,H] bf16 expert output
     uint16_t* y;                // [T,H] bf16 layer output
     int* ctl;                   // kCtlInts control ints, zero at launch
-    int* status;                // bit 0: a wait ran past its bound
+    int* status;                // kStatus* bits
+    long long wait_ticks;       // bound of every wait, in ticks of the 100 MHz real-time counter
     long long R;
     int T, H, F, K, E, apply;
 };
 
 __global__ __launch_bounds__(256) void k_decode_reset(int* __restrict__ ctl, int n, int* __restrict__ status) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) ctl[i] = 0;
-    if (threadIdx.x == 0) status[0] = 0;
+    if (threadIdx.x == 0) status[0] &= kStatusAbort;
 }
 
 // Thread 0: wait until *c >= target (bounded).  (The branch is taken per
@@ -104,15 +109,15 @@ __global__ __launch_bounds__(256) void k_decode_reset(int* __restrict__ ctl, int
 // written on this one.
 __device__ __forceinline__ void wait_count(const DecodeArgs& a, int* c, int target, int wave, int lane) {
     if (wave == 0 && lane == 0) {
-        if (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
-            const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-                if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-                    __hip_atomic_fetch_or(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
+        // any status bit (a time-out elsewhere, or the caller's abort) ends every wait at once
+        const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+               __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if ((long long)__builtin_amdgcn_s_memrealtime() - t0 > a.wait_ticks) {
+                __hip_atomic_fetch_or(a.status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
             }
+            __builtin_amdgcn_s_sleep(2);
         }
     }
     __syncthreads();
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
     // producer and consumer of every F1 -> Q -> F2 dependency share an L2.
     const int q = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg(20 | (15 << 11)));   // XCC_ID[15:0]
     if (q >= kQueues) {
-        if (tid == 0) __hip_atomic_fetch_or(a.status, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_fetch_or(a.status, kStatusPlacement, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
@@ -285,7 +290,7 @@ size_t decode_layer_scratch_bytes(long long R, int H, int F) {
 
 hipError_t launch_decode_layer(const moe_handle* h, int F, const void* x, const void* w1, const float* w1s,
                                const void* w2, const float* w2s, void* scratch, void* expert_out, int apply_probs,
-                               void* y, int32_t* status, int num_cu, hipStream_t s) {
+                               void* y, int32_t* status, long long wait_ticks, int num_cu, hipStream_t s) {
     const moe_desc& d = h->desc;
     const long long R = d.out_rows;
     // the scratch regions of the fp8 expert MLP, then the control ints
@@ -309,6 +314,7 @@ hipError_t launch_decode_layer(const moe_handle* h, int F, const void* x, const 
     a.eo = (uint16_t*)expert_out;
     a.y = (uint16_t*)y;
     a.status = status;
+    a.wait_ticks = wait_ticks;
     a.R = R;
     a.T = d.T;
     a.H = d.H;

@@ -102,6 +102,6 @@ hipError_t launch_decode_fused(const moe_handle* h, int F, const void* x, const 
                                void* y, int num_cu, hipStream_t s);
 hipError_t launch_decode_layer(const moe_handle* h, int F, const void* x, const void* w1, const float* w1s,
                                const void* w2, const float* w2s, void* scratch, void* expert_out, int apply_probs,
-                               void* y, int32_t* status, int num_cu, hipStream_t s);
+                               void* y, int32_t* status, long long wait_ticks, int num_cu, hipStream_t s);
 
 }  // namespace moe

@@ -337,15 +337,27 @@ int moe_combine_fp8(const moe_handle* h, const void* d_expert_out_q, const float
  *   d_expert_out   [R,H] bf16, caller-owned and reused; rows holding no kept
  *                  copy are unspecified
  *   d_y            [T,H] bf16 out
- *   d_status       [1] int32 out, written fresh: 0, or bit 0 set if a wait of
- *                  the kernel ran past its bound (0.25 s), bit 1 set if a
- *                  workgroup ran on an XCD numbered 8 or more (the work queues
- *                  assume XCDs 0-7); the outputs are then unspecified.  The
- *                  kernel always runs to its end. */
+ *   d_status       [1] int32 in/out.  The call clears bits 0 and 1 and keeps
+ *                  bit 2.  On return: bit 0 set if a wait of the kernel ran
+ *                  past its bound (0.25 s, see moe_decode_layer_set_wait_bound),
+ *                  bit 1 set if a workgroup ran on an XCD numbered 8 or more
+ *                  (the work queues assume XCDs 0-7); the outputs are then
+ *                  unspecified.  Bit 2 is the caller's abort request: set
+ *                  before the call, or while the kernel runs (e.g. by a copy
+ *                  on another stream), it makes every wait return at once;
+ *                  the outputs are then unspecified.  Once any bit is set,
+ *                  every later wait returns at once, so the kernel always runs
+ *                  to its end. */
 size_t moe_decode_layer_scratch_bytes(const moe_handle* h, int32_t F);
 int moe_decode_layer_fp8(const moe_handle* h, int32_t F, const void* d_x, const void* d_w1, const float* d_w1_scales,
                          const void* d_w2, const float* d_w2_scales, void* d_scratch, size_t scratch_bytes,
                          void* d_expert_out, int32_t apply_probs, void* d_y, int32_t* d_status, void* stream);
+
+/* Bound of every wait of moe_decode_layer_fp8, in ticks of the GPU's 100 MHz
+ * real-time counter, for calls made after this one in the process; ticks <= 0
+ * restores the default (25,000,000 = 0.25 s).  For tests of the time-out
+ * path and for callers that want a failed dependency reported sooner. */
+void moe_decode_layer_set_wait_bound(int64_t ticks);
 
 /* ---- fused decode layer ------------------------------------------------------------
  * [P5] first commit message (dispatch, FC1, FC2 and combine of a decode batch

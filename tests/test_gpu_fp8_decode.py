@@ -7,6 +7,7 @@ import torch
 
 import moe_synth as S
 import oracle
+import combine_routing_preprocess_amd._abi as A
 from combine_routing_preprocess_amd import Dispatcher
 from gpu_util import DEV, dev, host_bf16, log, rel_l2, require_clear_flag, row_rel_l2
 
@@ -140,13 +141,15 @@ def test_decode_graph_replay_matches_eager(fp8_weights):
             assert int(d.flag.item()) == 0
 
 
-def _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, scratch=None):
-    """preprocess + the persistent decode layer; returns (y, expert_out, status)."""
+def _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, scratch=None, status_init=3):
+    """preprocess + the persistent decode layer; returns (y, expert_out,
+    status).  The status word starts at `status_init` (bits 0 and 1 are
+    cleared by the call, bit 2 is the caller's abort request)."""
     scratch = scratch if scratch is not None else torch.empty(d.decode_layer_scratch_bytes(c.F), dtype=torch.uint8,
                                                               device=DEV)
     eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
     y = torch.full((d.T, c.H), 7.0, dtype=torch.bfloat16, device=DEV)
-    st = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    st = torch.full((1,), status_init, dtype=torch.int32, device=DEV)
     d.preprocess(dev(idx), dev(pr), tl)
     d.decode_layer_fp8(dev(x), w1q, w2q, w1s, w2s, scratch=scratch, expert_out=eo, out=y, status=st)
     return y, eo, st
@@ -222,6 +225,37 @@ def test_decode_megakernel_graph_replay_and_empty_batch(fp8_weights):
                 assert torch.count_nonzero(yb.float()).item() == 0
 
 
+def test_decode_megakernel_abort_and_wait_bound(fp8_weights):
+    """Failure handling forced from the host, each call ending normally: the
+    caller's abort bit makes every wait return at once (the status keeps
+    bit 2 and gains nothing else); a wait bound of one tick makes waits run
+    past it (status bit 0); the next call, with the default bound and a clear
+    status, is bit-identical to the separate launches."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    bucket, idx, pr, x = _decode_case(c, 16)
+    tl = torch.tensor([16], dtype=torch.int32, device=DEV)
+    d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    log("decode megakernel abort")
+    _, _, st = _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, status_init=4)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 4
+    log("decode megakernel wait bound 1 tick")
+    A.lib().moe_decode_layer_set_wait_bound(1)
+    try:
+        _, _, st = _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, status_init=0)
+        torch.cuda.synchronize()
+    finally:
+        A.lib().moe_decode_layer_set_wait_bound(0)
+    assert int(st.item()) & 3 == 1
+    log("decode megakernel after the forced failures")
+    y, _, st = _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, status_init=0)
+    d2 = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    y2 = d2.layer(dev(x), dev(idx), dev(pr), w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("T,H,E,K,F,pad", [(33, 256, 8, 2, 256, 16), (1, 128, 4, 1, 128, 1), (70, 384, 5, 3, 128, 8)])
 def test_decode_megakernel_small_shapes(T, H, E, K, F, pad):
     """Small shapes, ragged expert counts: bit-identical to the separate
@@ -236,7 +270,7 @@ def test_decode_megakernel_small_shapes(T, H, E, K, F, pad):
     scr = torch.empty(d.decode_layer_scratch_bytes(F), dtype=torch.uint8, device=DEV)
     eo = torch.empty((d.R, H), dtype=torch.bfloat16, device=DEV)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
-    st = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    st = torch.full((1,), 3, dtype=torch.int32, device=DEV)
     d.preprocess(dev(idx), dev(pr))
     d.decode_layer_fp8(dev(x), W[0], W[2], W[1], W[3], scratch=scr, expert_out=eo, out=y, status=st)
     d2 = Dispatcher(T, H, E, K, pad_multiple=pad)
