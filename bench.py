@@ -532,9 +532,14 @@ def run_decode(args):
             d.preprocess(rt, pt, tl)
             d.decode_layer_fp8(x, w1q, w2q, w1s, w2s, scratch=scr, expert_out=eo, out=y, status=status)
     else:
+        # routing, quantise-on-dispatch, FC1, row quantiser, FC2, combine
+        d = Dispatcher(T, c.H, c.E, c.K, pad_multiple=c.pad, payload="fp8")
+        perm = torch.empty((d.R, c.H), dtype=torch.uint8, device=dev)
+        perm_s = torch.empty((d.R, c.H // 128), dtype=torch.float32, device=dev)
+
         def step():
-            d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, scratch=scr, expert_out=eo,
-                    out=y, T_live=tl, check_overflow=True)
+            d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, perm_scales=perm_s, scratch=scr,
+                    expert_out=eo, out=y, T_live=tl, check_overflow=True)
 
     _require_clear_flag(d, rt, pt, tl)
     for _ in range(args.warmup):
@@ -674,14 +679,16 @@ def run_workloads():
     for T in (16, 64, 256):
         idx, pr = S.route_sigmoid_topk(T, c.E, c.K, c.seed + T)
         x = torch.from_numpy(S.bf16_normal((T, c.H), c.seed + T).view(np.int16)).to(dev).view(torch.bfloat16)
-        d = Dispatcher(T, c.H, c.E, c.K, pad_multiple=c.pad)
+        # separate launches: routing, quantise-on-dispatch, FC1, row quantiser, FC2, combine
+        d = Dispatcher(T, c.H, c.E, c.K, pad_multiple=c.pad, payload="fp8")
         rt, pt = torch.from_numpy(idx).to(dev), torch.from_numpy(pr).to(dev)
-        perm = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
+        perm = torch.empty((d.R, c.H), dtype=torch.uint8, device=dev)
+        perm_s = torch.empty((d.R, c.H // 128), dtype=torch.float32, device=dev)
         scr = d.alloc_mlp_scratch(c.F, "fp8")
         eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=dev)
         y = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
-        step = lambda: d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, scratch=scr,
-                               expert_out=eo, out=y, check_overflow=True)
+        step = lambda: d.layer(x, rt, pt, w1q, w2q, w1_scales=w1s, w2_scales=w2s, perm=perm, perm_scales=perm_s,
+                               scratch=scr, expert_out=eo, out=y, check_overflow=True)
         _require_clear_flag(d, rt, pt)
         gm, gmed = _graph_times(step)
         touched = int((oracle.route(idx, 0, c.E, c.K, pr, c.pad)["counts"] > 0).sum())
@@ -728,7 +735,7 @@ def run_workloads():
                                         "weight_GB_s": round(wbytes / (pm * 1e-3) / 1e9, 1),
                                         "frac_of_hbm_roofline": round(wbytes / (pm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                         "bit_identical_to_separate": psame, "status": pstatus}}
-        del d, perm, scr, eo, y, df, fscr, feo, fy, dp, pscr, peo, py, pst
+        del d, perm, perm_s, scr, eo, y, df, fscr, feo, fy, dp, pscr, peo, py, pst
     res["decode_fp8_7168_e256"] = out5
     del w1q, w1s, w2q, w2s
     torch.cuda.empty_cache()

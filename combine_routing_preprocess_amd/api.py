@@ -518,15 +518,23 @@ class Dispatcher:
                 "moe_decode_fused_fp8")
         return out
 
-    def layer(self, x, routing, probs, w1, w2, *, perm=None, scratch=None, expert_out=None, out=None,
-              w1_scales=None, w2_scales=None, T_live=None, apply_probs=True, check_overflow=False):
-        """dispatch -> grouped MLP -> combine on the current stream.  With
-        ``check_overflow``, a device-side assert on the overflow flag is
-        enqueued after the combine (no host wait; capturable).  Buffers the
-        caller omits are allocated per call."""
-        perm, _, flag, _, _ = self.dispatch(x, routing, probs, out=perm, T_live=T_live)
+    def layer(self, x, routing, probs, w1, w2, *, perm=None, perm_scales=None, scratch=None, expert_out=None,
+              out=None, w1_scales=None, w2_scales=None, T_live=None, apply_probs=True, check_overflow=False):
+        """dispatch -> grouped MLP -> combine on the current stream.  With a
+        handle of fp8 payload and bf16 tokens, dispatch quantises on the way
+        (routing metadata, then moe_permute_quantize into e4m3 rows ``perm``
+        with 1x128 scales ``perm_scales``).  With ``check_overflow``, a
+        device-side assert on the overflow flag is enqueued after the combine
+        (no host wait; capturable).  Buffers the caller omits are allocated
+        per call."""
+        if self.payload == A.FP8E4M3_B128 and x.dtype == torch.bfloat16:
+            _, flag = self.preprocess(routing, probs, T_live)
+            perm, perm_scales = self.permute_quantize(x, out=perm, out_scales=perm_scales)
+        else:
+            perm, _, flag, _, perm_scales = self.dispatch(x, routing, probs, out=perm, out_scales=perm_scales,
+                                                          T_live=T_live)
         y = self.grouped_mlp(perm, w1, w2, w1_scales=w1_scales, w2_scales=w2_scales, scratch=scratch,
-                             out=expert_out)
+                             out=expert_out, perm_scales=perm_scales)
         y = self.combine(y, apply_probs=apply_probs, out=out)
         if check_overflow:
             assert_no_overflow(flag)

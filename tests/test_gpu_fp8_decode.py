@@ -141,6 +141,26 @@ def test_decode_graph_replay_matches_eager(fp8_weights):
             assert int(d.flag.item()) == 0
 
 
+@pytest.mark.parametrize("T", [16, 100])
+def test_layer_quantise_on_dispatch_matches_permute_then_quantise(fp8_weights, T):
+    """layer() on a handle of fp8 payload (routing metadata, quantise-on-
+    dispatch, fp8 grouped MLP, combine) equals layer() on a bf16 handle
+    (permute, row quantiser, fp8 grouped MLP, combine) bit for bit, live
+    count below the bucket included."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    bucket, idx, pr, x = _decode_case(c, T)
+    log("layer quantise-on-dispatch", T, bucket)
+    tl = torch.tensor([T], dtype=torch.int32, device=DEV)
+    d8 = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad, payload="fp8")
+    y8 = d8.layer(dev(x), dev(idx), dev(pr), w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl,
+                  check_overflow=True)
+    d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad)
+    y = d.layer(dev(x), dev(idx), dev(pr), w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl)
+    torch.cuda.synchronize()
+    assert int(d8.flag.item()) == 0
+    assert torch.equal(y8.view(torch.int16), y.view(torch.int16))
+
+
 def _megakernel_case(c, d, x, idx, pr, tl, w1q, w1s, w2q, w2s, scratch=None, status_init=3):
     """preprocess + the persistent decode layer; returns (y, expert_out,
     status).  The status word starts at `status_init` (bits 0 and 1 are
