@@ -8,7 +8,8 @@
 // "perf(moe): sync-free HybridEP dispatch" (sections "What does this PR do ?",
 // "Validation").
 //
-// Three launches, all graph-capturable and free of memsets:
+// Three launches, all graph-capturable and free of memsets (batches of up to
+// 256 tokens with dense routing take one, k_route_small, below):
 //  1. k_route_tiles  -- one wavefront per 64-token tile.  Every tile builds a
 //     64-bit membership mask per expert in LDS (bit l = token l of the tile
 //     routes to the expert).  popcount(mask) is the tile's count for that
@@ -342,6 +343,182 @@ __global__ __launch_bounds__(256) void k_route_assign(
     }
 }
 
+// Small batches (at most kSmallTiles tiles, i.e. T <= 256) with dense
+// routing: the three steps above in one workgroup of 1024 threads, the tile
+// masks and bases in LDS.  Decode batches pay one launch instead of three.
+// Wavefront w builds tile w's masks exactly as k_route_tiles does (each
+// lane's slots in order, so its ranks and duplicate bits are the same), one
+// thread per expert scans the tiles and the experts as k_route_scan does,
+// wavefront w assigns tile w's slots as k_route_assign does, and every thread
+// takes a share of the rows without a copy.  Integer arithmetic throughout,
+// so every output equals the three-launch path's.
+constexpr int kSmallTiles = 4;
+constexpr long long kSmallRows = 16384;    // rows past this go to the three-launch fill
+
+template <int FMT>
+__global__ __launch_bounds__(1024) void k_route_small(const void* __restrict__ routing,
+                                                      const float* __restrict__ probs,
+                                                      const int32_t* __restrict__ T_live_ptr, int T, int E, int K,
+                                                      int pad, int cap, long long R, int n_tiles,
+                                                      int32_t* __restrict__ row_id, float* __restrict__ copy_prob,
+                                                      int32_t* __restrict__ counts_out,
+                                                      int32_t* __restrict__ kept_out, int64_t* __restrict__ seg_off,
+                                                      int64_t* __restrict__ rows_needed,
+                                                      int32_t* __restrict__ src_row, float* __restrict__ out_probs,
+                                                      int32_t* __restrict__ flag) {
+    static_assert(FMT != MOE_ROUTE_SPARSE_BOOL, "dense routing only");
+    __shared__ unsigned long long msk[kSmallTiles][kMaxE];
+    __shared__ int tbase[kSmallTiles][kMaxE];
+    __shared__ long long s_off[kMaxE + 1];
+    __shared__ int s_kept[kMaxE];
+    __shared__ long long scan[16];
+    __shared__ int sflag;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int T_live = T;
+    if (T_live_ptr) T_live = min(max(*T_live_ptr, 0), T);
+    for (int i = tid; i < n_tiles * E; i += 1024) msk[i / E][i % E] = 0ull;
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+
+    // 1. membership masks of tile wv (lane = token), slot expert ids and probabilities
+    const int t = wv * kTileTok + lane;
+    const bool mine = wv < n_tiles && t < T;
+    int err = 0;
+    constexpr int U = 8;                   // slots loaded together, so their latencies overlap
+    if (mine) {
+        const bool live = t < T_live;
+        const unsigned long long bit = 1ull << lane;
+        for (int j0 = 0; j0 < K; j0 += U) {
+            int ev[U];
+            float pv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const size_t at = (size_t)t * K + min(j0 + u, K - 1);
+                ev[u] = (FMT == MOE_ROUTE_DENSE_I16) ? (int)((const int16_t*)routing)[at]
+                                                     : ((const int32_t*)routing)[at];
+                pv[u] = probs ? probs[at] : 1.f;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u >= K) break;
+                const size_t at = (size_t)t * K + j0 + u;
+                const int e = ev[u];
+                int oute = -1;
+                float p = 0.f;
+                if (live && e != -1) {
+                    if (e < -1 || e >= E) {
+                        err |= MOE_FLAG_BAD_EXPERT;
+                    } else {
+                        // this lane alone sets bit `lane`, walking its slots in
+                        // order: the old value says whether e occurred earlier
+                        const unsigned long long old = atomicOr(&msk[wv][e], bit);
+                        if (old & bit) {
+                            err |= MOE_FLAG_DUPLICATE;
+                        } else {
+                            oute = e;
+                            p = pv[u];
+                        }
+                    }
+                }
+                row_id[at] = oute;
+                copy_prob[at] = p;
+            }
+        }
+    }
+    if (err) atomicOr(&sflag, err);
+    __syncthreads();
+
+    // 2. per expert: tile bases, count, capacity, padding; exclusive scan over experts
+    long long padded = 0;
+    if (tid < E) {
+        int run = 0;
+        for (int tl = 0; tl < n_tiles; ++tl) {
+            tbase[tl][tid] = run;
+            run += __popcll(msk[tl][tid]);
+        }
+        int kept = run;
+        if (cap >= 0 && run > cap) {
+            kept = cap;
+            atomicOr(&sflag, MOE_FLAG_CAPACITY);
+        }
+        counts_out[tid] = run;
+        kept_out[tid] = kept;
+        s_kept[tid] = kept;
+        padded = ((long long)kept + pad - 1) / pad * pad;
+    }
+    long long incl = padded;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const long long v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+    }
+    if (lane == 63) scan[wv] = incl;
+    __syncthreads();
+    long long before = 0;
+    for (int w2 = 0; w2 < wv; ++w2) before += scan[w2];
+    incl += before;
+    if (tid < E) {
+        s_off[tid] = incl - padded;
+        seg_off[tid] = incl - padded;
+    }
+    if (tid == E - 1) {
+        s_off[E] = incl;
+        seg_off[E] = incl;
+        *rows_needed = incl;
+        if (incl > R) atomicOr(&sflag, MOE_FLAG_OUT_ROWS);
+    }
+    __syncthreads();
+
+    // 3. final rows of tile wv's slots (each thread re-reads only its own slots)
+    if (mine) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+        for (int j0 = 0; j0 < K; j0 += U) {
+            int ev[U];
+            float pv[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const size_t at = (size_t)t * K + min(j0 + u, K - 1);
+                ev[u] = row_id[at];
+                pv[u] = copy_prob[at];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u >= K) break;
+                const int e = ev[u];
+                if (e < 0) continue;
+                const size_t at = (size_t)t * K + j0 + u;
+                const int rank = tbase[wv][e] + __popcll(msk[wv][e] & below);
+                const long long row = s_off[e] + rank;
+                if (rank < s_kept[e] && row < R) {
+                    row_id[at] = (int)row;
+                    src_row[row] = t;
+                    if (out_probs) out_probs[row] = pv[u];
+                } else {
+                    row_id[at] = -1;
+                    copy_prob[at] = 0.f;
+                }
+            }
+        }
+    }
+    // 4. rows that hold no copy: padding inside segments, everything past the last one
+    for (long long r = tid; r < R; r += 1024) {
+        bool assigned = false;
+        if (r < s_off[E]) {
+            int lo = 0, hi = E - 1;              // last e with s_off[e] <= r
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            assigned = r < s_off[lo] + s_kept[lo];
+        }
+        if (!assigned) {
+            src_row[r] = -1;
+            if (out_probs) out_probs[r] = 0.f;
+        }
+    }
+    if (tid == 0) *flag = sflag;
+}
+
 }  // namespace
 
 hipError_t launch_route(const moe_handle* h, const void* routing, const float* probs,
@@ -349,6 +526,19 @@ hipError_t launch_route(const moe_handle* h, const void* routing, const float* p
                         int32_t* flag, hipStream_t s) {
     const moe_desc& d = h->desc;
     const int nt = h->n_tiles;
+    if (nt <= kSmallTiles && d.out_rows <= kSmallRows && d.route_fmt != MOE_ROUTE_SPARSE_BOOL) {
+        if (d.route_fmt == MOE_ROUTE_DENSE_I16)
+            hipLaunchKernelGGL(k_route_small<MOE_ROUTE_DENSE_I16>, dim3(1), dim3(1024), 0, s, routing, probs, T_live,
+                               d.T, d.E, d.K, d.pad_multiple, d.capacity, (long long)d.out_rows, nt, h->row_id,
+                               h->copy_prob, tokens_per_expert, h->kept, h->seg_off, h->rows_needed, h->src_row,
+                               out_probs, flag);
+        else
+            hipLaunchKernelGGL(k_route_small<MOE_ROUTE_DENSE_I32>, dim3(1), dim3(1024), 0, s, routing, probs, T_live,
+                               d.T, d.E, d.K, d.pad_multiple, d.capacity, (long long)d.out_rows, nt, h->row_id,
+                               h->copy_prob, tokens_per_expert, h->kept, h->seg_off, h->rows_needed, h->src_row,
+                               out_probs, flag);
+        return hipGetLastError();
+    }
     if (nt > 0) {
         switch (d.route_fmt) {
             case MOE_ROUTE_DENSE_I16:
