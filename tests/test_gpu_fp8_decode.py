@@ -276,6 +276,48 @@ def test_decode_megakernel_abort_and_wait_bound(fp8_weights):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("apply_probs", [True, False])
+def test_decode_megakernel_sparse_routing_and_capacity(apply_probs):
+    """The persistent decode layer on a Boolean routing map with a capacity
+    that drops copies (some tokens lose all of theirs, and their rows must
+    come out zero): bit-identical to the separate launches on the same
+    handle state, with and without the probability weights, against the
+    oracle, and with a clear status."""
+    T, H, E, K, F, pad, cap = 48, 256, 6, 3, 256, 8, 20
+    idx, pr = S.route_softmax_topk(T, E, K, 77)
+    smap, sprob = S.dense_to_sparse(idx, E, pr)
+    x = S.bf16_normal((T, H), 78)
+    w1q, w1s = S.weights_fp8_blocks(E, 2 * F, H, 79, std=0.05)
+    w2q, w2s = S.weights_fp8_blocks(E, H, F, 80, std=0.05)
+    W = [t.to(DEV) for t in (w1q, w1s, w2q, w2s)]
+    log("decode megakernel sparse", apply_probs)
+    d = Dispatcher(T, H, E, K, route_fmt="sparse_bool", pad_multiple=pad, capacity=cap)
+    scr = torch.empty(d.decode_layer_scratch_bytes(F), dtype=torch.uint8, device=DEV)
+    eo = torch.zeros((d.R, H), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((T, H), 7.0, dtype=torch.bfloat16, device=DEV)
+    st = torch.full((1,), 3, dtype=torch.int32, device=DEV)
+    d.preprocess(dev(smap), dev(sprob))
+    d.decode_layer_fp8(dev(x), W[0], W[2], W[1], W[3], scratch=scr, expert_out=eo, out=y, status=st,
+                       apply_probs=apply_probs)
+    d2 = Dispatcher(T, H, E, K, route_fmt="sparse_bool", pad_multiple=pad, capacity=cap)
+    perm, *_ = d2.dispatch(dev(x), dev(smap), dev(sprob))
+    eo2 = d2.grouped_mlp(perm, W[0], W[2], w1_scales=W[1], w2_scales=W[3])
+    y2 = d2.combine(eo2, apply_probs=apply_probs)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert int(d.flag.item()) & 1                      # the capacity dropped copies
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    kept_rows = (d.src_row >= 0).nonzero().flatten()
+    assert torch.equal(eo[kept_rows].view(torch.int16), eo2[kept_rows].view(torch.int16))
+    rt = oracle.route(smap, oracle.FMT_SPARSE_U8, E, K, sprob, pad, cap, d.R)
+    want = oracle.layer_tokens(np.arange(T), x, rt, lambda e, rows: oracle.expert_mlp_fp8(
+        rows, w1q[e].numpy(), w1s[e].numpy(), w2q[e].numpy(), w2s[e].numpy()), apply_probs=apply_probs)
+    _check(host_bf16(y), want, "megakernel sparse")
+    none = (rt["row_id"] < 0).all(axis=1)
+    assert none.any()
+    assert torch.count_nonzero(y[torch.from_numpy(np.nonzero(none)[0]).to(DEV)].float()).item() == 0
+
+
 @pytest.mark.parametrize("T,H,E,K,F,pad", [(33, 256, 8, 2, 256, 16), (1, 128, 4, 1, 128, 1), (70, 384, 5, 3, 128, 8)])
 def test_decode_megakernel_small_shapes(T, H, E, K, F, pad):
     """Small shapes, ragged expert counts: bit-identical to the separate
