@@ -14,10 +14,11 @@
 //
 // Work items, in their global order (every dependency points to an earlier
 // item):
-//   D(t)     quantise token row t and write it to each kept copy's row
-//   F1(a,u)  FC1 + SwiGLU unit u of the a-th expert holding rows   needs all D
+//   D(t,h)   quantise column groups 4h..4h+3 of token row t into each
+//            kept copy's row (one group of 1024 columns per wavefront)
+//   F1(a,u)  FC1 + SwiGLU units of the a-th expert holding rows     needs all D
 //   Q(a)     quantise that expert's activation rows                 needs its F1
-//   F2(a,u)  FC2 unit u of the expert                               needs its Q
+//   F2(a,u)  FC2 units of the expert                                needs its Q
 //   C(t)     combine of token t                                     needs all F2
 // Items are spread over 8 queues, one per XCD (tokens t % 8, experts a % 8);
 // a workgroup takes tickets from the queue of the XCD it runs on (hardware
@@ -37,10 +38,13 @@
 //   * F1 and Q items (read only on their own XCD) are counted with relaxed
 //     increments, and their readers, after seeing the count, invalidate only
 //     the CU's L1 (buffer_inv sc0): the data are in the shared L2;
-//   * D items (token rows read on every XCD) are counted with release
-//     increments at agent scope (L2 written back); each workgroup takes one
-//     acquire at agent scope (L2 and L1 invalidated) before its first F1
-//     item, after the count shows every D item done;
+//   * D items (token rows read on every XCD) are counted per queue with
+//     relaxed increments; the increment that completes a queue writes back
+//     the XCD's L2 (release at agent scope) and counts the queue.  Before its
+//     first F1 item a workgroup waits for every queue with D items; then the
+//     first workgroup of each XCD to get there invalidates the XCD's L2
+//     (acquire at agent scope) and marks it done, and the others wait for
+//     that mark (its owner waits on nothing) and invalidate their CU's L1;
 //   * F2 items are counted per queue with relaxed increments; the increment
 //     that completes a queue writes back the XCD's L2 (release at agent scope,
 //     covering every F2 item of the queue) and counts the queue; C items wait
@@ -67,9 +71,17 @@ constexpr int kCtlFc2 = kCtlDispatch + kCtlStride;    // queues whose F2 items a
 constexpr int kCtlFc1 = kCtlFc2 + kCtlStride;         // F1 items done, per active expert
 constexpr int kCtlQuant = kCtlFc1 + kMaxE;            // Q item done, per active expert
 constexpr int kCtlFc2Q = kCtlQuant + kMaxE;           // F2 items done, per queue
-constexpr int kCtlInts = kCtlFc2Q + kQueues * kCtlStride;
+constexpr int kCtlDispQ = kCtlFc2Q + kQueues * kCtlStride;   // D items done, per queue
+constexpr int kCtlDinv = kCtlDispQ + kQueues * kCtlStride;   // per queue: 1 = its XCD's L2 being invalidated, 2 = done
+constexpr int kCtlInts = kCtlDinv + kQueues * kCtlStride;
+// fp8 GEMM units per F1 / F2 item: fewer, larger items spend fewer claims,
+// polls and publications per byte of weights streamed
+#ifndef MOE_DECODE_UNITS_PER_ITEM
+#define MOE_DECODE_UNITS_PER_ITEM 2
+#endif
+constexpr int kUnitsPerItem = MOE_DECODE_UNITS_PER_ITEM;
 // how a finished item is published (see the claim loop)
-constexpr int kPubRelease = 1, kPubLocal = 2, kPubFc2 = 3;
+constexpr int kPubLocal = 2, kPubFc2 = 3, kPubDisp = 4;
 // status bits: a wait ran past its bound; a workgroup ran on an XCD numbered
 // 8 or more; the caller's abort request (kept by the reset)
 constexpr int kStatusTimeout = 1, kStatusPlacement = 2, kStatusAbort = 4;
@@ -161,6 +173,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char s_w[4 * kWaveLds];   // weight buffer per wavefront
     __shared__ int s_cnt;
     __shared__ int s_ticket;
+    __shared__ int s_flag;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // The queue is this workgroup's XCD (hardware register XCC_ID), so the
@@ -192,11 +205,15 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
     __syncthreads();
     const int n_act = s_cnt;
     const int upe1 = a.F / kFeat, upe2 = a.H / kFeat2;
-    // this queue's items: tokens q, q+8, ...; active experts q, q+8, ...
-    const int nD = a.T > q ? (a.T - q + kQueues - 1) / kQueues : 0;
-    const int nA = n_act > q ? (n_act - q + kQueues - 1) / kQueues : 0;
-    const int eF1 = nD + nA * upe1, eQ = eF1 + nA, eF2 = eQ + nA * upe2, eC = eF2 + nD;
     const int nbH = a.H / 128, ngH = (nbH + kPQBlocks - 1) / kPQBlocks;
+    // this queue's items: tokens q, q+8, ...; active experts q, q+8, ...
+    const int nTq = a.T > q ? (a.T - q + kQueues - 1) / kQueues : 0;
+    const int dpt = (ngH + 3) / 4;       // D items per token: four column groups each, one per wavefront
+    const int nD = nTq * dpt;
+    const int nA = n_act > q ? (n_act - q + kQueues - 1) / kQueues : 0;
+    // items per expert: runs of kUnitsPerItem consecutive units (the last may be shorter)
+    const int ipe1 = (upe1 + kUnitsPerItem - 1) / kUnitsPerItem, ipe2 = (upe2 + kUnitsPerItem - 1) / kUnitsPerItem;
+    const int eF1 = nD + nA * ipe1, eQ = eF1 + nA, eF2 = eQ + nA * ipe2, eC = eF2 + nTq;
     const int nbF = a.F / 128, ngF = (nbF + kQBlocks - 1) / kQBlocks;
     int* ctl = a.ctl;
 
@@ -208,8 +225,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
         if (wave == 0) {
             int tk = 0;
             if (lane == 0) {
-                if (pub == kPubRelease) {
-                    __hip_atomic_fetch_add(done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                if (pub == kPubDisp) {
+                    if (__hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nD - 1)
+                        __hip_atomic_fetch_add(ctl + kCtlDispatch, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
                 } else if (pub == kPubLocal) {
                     __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 } else if (pub == kPubFc2) {
@@ -227,29 +245,54 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
         __syncthreads();                 // s_ticket is rewritten by the next claim
         if (i >= eC) break;
         if (i < nD) {
-            // D(t): quantise-on-dispatch of token t
-            const long long t = q + (long long)kQueues * i;
-            for (int g = wave; g < ngH; g += 4)
-                permute_quant_wave(a.x, a.H, a.K, (int)a.R, a.row_id, a.xq, a.xs, t, g * kPQBlocks, lane);
+            // D(t, h): quantise-on-dispatch of token t, column groups 4h .. 4h+3 (one per wavefront)
+            const long long t = q + (long long)kQueues * (i / dpt);
+            const int g = 4 * (i % dpt) + wave;
+            if (g < ngH) permute_quant_wave(a.x, a.H, a.K, (int)a.R, a.row_id, a.xq, a.xs, t, g * kPQBlocks, lane);
             finish_item();
-            done = ctl + kCtlDispatch;
-            pub = kPubRelease;
+            done = ctl + kCtlDispQ + q * kCtlStride;
+            pub = kPubDisp;
         } else if (i < eF1) {
-            const int k = i - nD, ai = q + kQueues * (k / upe1), u = k % upe1;
+            const int k = i - nD, ai = q + kQueues * (k / ipe1), u0 = (k % ipe1) * kUnitsPerItem;
             if (!__builtin_amdgcn_readfirstlane(have_d)) {   // token rows never change after the D items: acquire once
-                wait_count(a, ctl + kCtlDispatch, a.T, wave, lane);
-                acquire_agent();
+                // every queue with D items has written them back; then one
+                // workgroup per XCD invalidates the XCD's L2, and the others
+                // wait for it (it waits on nothing) and invalidate their L1
+                wait_count(a, ctl + kCtlDispatch, min(a.T, kQueues), wave, lane);
+                int* dinv = ctl + kCtlDinv + q * kCtlStride;
+                if (wave == 0) {
+                    int first = 0;
+                    if (lane == 0) {
+                        int expect = 0;
+                        first = __hip_atomic_compare_exchange_strong(dinv, &expect, 1, __ATOMIC_RELAXED,
+                                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    s_flag = __builtin_amdgcn_readfirstlane(first);
+                }
+                __syncthreads();
+                const int first = __builtin_amdgcn_readfirstlane(s_flag);
+                __syncthreads();
+                if (first) {
+                    acquire_agent();
+                    __syncthreads();
+                    if (wave == 0 && lane == 0)
+                        __hip_atomic_store(dinv, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    wait_count(a, dinv, 2, wave, lane);
+                    acquire_local();
+                }
                 have_d = true;
             }
-            fp8_unit<0>(a.xq, a.xs, a.w1, a.w1s, a.act, a.seg_off, a.kept, a.R, a.H, 2 * a.F, a.F, s_list[ai], u,
-                        lane, wave, s_w + wave * kWaveLds);
+            for (int u = u0; u < min(upe1, u0 + kUnitsPerItem); ++u)
+                fp8_unit<0>(a.xq, a.xs, a.w1, a.w1s, a.act, a.seg_off, a.kept, a.R, a.H, 2 * a.F, a.F, s_list[ai], u,
+                            lane, wave, s_w + wave * kWaveLds);
             finish_item();
             done = ctl + kCtlFc1 + ai;
             pub = kPubLocal;
         } else if (i < eQ) {
             // Q(a): the expert's activation rows, (row, 8-block group) per wavefront
             const int ai = q + kQueues * (i - eF1), e = s_list[ai];
-            wait_count(a, ctl + kCtlFc1 + ai, upe1, wave, lane);
+            wait_count(a, ctl + kCtlFc1 + ai, ipe1, wave, lane);
             acquire_local();
             const long long seg = a.seg_off[e];
             long long me = a.kept[e];
@@ -260,11 +303,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_layer(DecodeArgs a) {
             done = ctl + kCtlQuant + ai;
             pub = kPubLocal;
         } else if (i < eF2) {
-            const int k = i - eQ, ai = q + kQueues * (k / upe2), u = k % upe2;
+            const int k = i - eQ, ai = q + kQueues * (k / ipe2), u0 = (k % ipe2) * kUnitsPerItem;
             wait_count(a, ctl + kCtlQuant + ai, 1, wave, lane);
             acquire_local();
-            fp8_unit<1>(a.aq, a.as, a.w2, a.w2s, a.eo, a.seg_off, a.kept, a.R, a.F, a.H, a.H, s_list[ai], u, lane,
-                        wave, s_w + wave * kWaveLds);
+            for (int u = u0; u < min(upe2, u0 + kUnitsPerItem); ++u)
+                fp8_unit<1>(a.aq, a.as, a.w2, a.w2s, a.eo, a.seg_off, a.kept, a.R, a.F, a.H, a.H, s_list[ai], u, lane,
+                            wave, s_w + wave * kWaveLds);
             finish_item();
             done = ctl + kCtlFc2Q + q * kCtlStride;
             pub = kPubFc2;
