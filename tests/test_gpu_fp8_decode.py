@@ -318,6 +318,46 @@ def test_decode_megakernel_sparse_routing_and_capacity(apply_probs):
     assert torch.count_nonzero(y[torch.from_numpy(np.nonzero(none)[0]).to(DEV)].float()).item() == 0
 
 
+def test_decode_megakernel_random_batches_back_to_back(fp8_weights):
+    """Ten decode batches at the full layer width, one after another on the
+    same scratch, expert-output and output buffers: random live counts
+    (1..256), softmax or Zipf-skewed routing, some with a capacity that
+    drops copies.  Each is bit-identical to the separate launches with a
+    clear status; the skewed ones pile many rows on a few experts, so
+    several passes over an expert's weights and uneven queues are covered."""
+    c, w1q, w1s, w2q, w2s = fp8_weights
+    r = np.random.default_rng(2024)
+    scr = eo = y = None
+    for case in range(10):
+        T = int(r.integers(1, 257))
+        bucket = S.next_pow2_bucket(T)
+        if case % 2:
+            idx, pr = S.route_zipf_gumbel(bucket, c.E, c.K, 500 + case)
+        else:
+            idx, pr = S.route_softmax_topk(bucket, c.E, c.K, 500 + case)
+        x = S.bf16_normal((bucket, c.H), 600 + case)
+        cap = int(r.integers(8, 40)) if case % 3 == 0 else None
+        log("decode megakernel random", case, T, bucket, cap)
+        tl = torch.tensor([T], dtype=torch.int32, device=DEV)
+        d = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad, capacity=cap)
+        need = d.decode_layer_scratch_bytes(c.F)
+        if scr is None or scr.numel() < need:
+            scr = torch.empty(need, dtype=torch.uint8, device=DEV)
+        if eo is None or eo.shape[0] < d.R:
+            eo = torch.empty((d.R, c.H), dtype=torch.bfloat16, device=DEV)
+        if y is None or y.shape[0] < bucket:
+            y = torch.empty((bucket, c.H), dtype=torch.bfloat16, device=DEV)
+        st = torch.full((1,), 3, dtype=torch.int32, device=DEV)
+        yv, eov = y[:bucket], eo[:d.R]
+        d.preprocess(dev(idx), dev(pr), tl)
+        d.decode_layer_fp8(dev(x), w1q, w2q, w1s, w2s, scratch=scr, expert_out=eov, out=yv, status=st)
+        d2 = Dispatcher(bucket, c.H, c.E, c.K, pad_multiple=c.pad, capacity=cap)
+        y2 = d2.layer(dev(x), dev(idx), dev(pr), w1q, w2q, w1_scales=w1s, w2_scales=w2s, T_live=tl)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, case
+        assert torch.equal(yv.view(torch.int16), y2.view(torch.int16)), case
+
+
 @pytest.mark.parametrize("T,H,E,K,F,pad", [(33, 256, 8, 2, 256, 16), (1, 128, 4, 1, 128, 1), (70, 384, 5, 3, 128, 8)])
 def test_decode_megakernel_small_shapes(T, H, E, K, F, pad):
     """Small shapes, ragged expert counts: bit-identical to the separate
