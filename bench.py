@@ -256,12 +256,7 @@ def main() -> int:
     workloads = None if args.no_workloads else run_workloads()
     extra = run_extra(args) if args.extra else None
     if args.calib_copy:
-        a = torch.empty(2 ** 29, dtype=torch.int16, device=dev)
-        a.fill_(1)
-        bq = torch.empty_like(a)
-        torch.cuda.synchronize()
-        bq.copy_(a)
-        torch.cuda.synchronize()
+        _calib_copy()
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -492,6 +487,18 @@ def _event_times(fn, reps=30, warm=5, flush=False):
     return min(t), st.median(t)
 
 
+def _calib_copy():
+    """One device-to-device copy of exactly 1 GiB: the reference dispatch that
+    scales hardware byte counters to bytes."""
+    import torch
+    a = torch.empty(2 ** 29, dtype=torch.int16, device="cuda")
+    a.fill_(1)
+    bq = torch.empty_like(a)
+    torch.cuda.synchronize()
+    bq.copy_(a)
+    torch.cuda.synchronize()
+
+
 def run_decode(args):
     """Decode-sized layer with fp8 weights, eager launches: routing metadata,
     permute, FC1 + SwiGLU, FC2, combine for `--tokens` live tokens in the
@@ -551,6 +558,8 @@ def run_decode(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     st = int(status.item())
+    if args.calib_copy:
+        _calib_copy()
     print(json.dumps({"workload": f"decode_fp8: {T_live} live tokens (bucket {T}) x {c.H}, {c.E} experts top-{c.K}, "
                                   f"FFN {c.F}, fp8 e4m3 weights", "path": args.decode_path,
                       "ms_per_layer_eager": round(ms, 4), "status": st,
