@@ -21,10 +21,15 @@
 //    lane are the gate and up values of one feature.  Longer segments, and
 //    FC2 into the fp8 format, cut them into chunks of 320 rows taken by two
 //    128-row passes (the token chunk is then read twice, from L2).
-//  * Experts are dealt to XCDs (expert e -> XCD e mod 8; workgroup b runs on
-//    XCD b mod 8).  The 32 workgroups of an XCD walk that XCD's units in
-//    order and move through K at the same pace, so a token slice comes from
-//    HBM once and is then served by the XCD's L2.
+//  * The units of all experts, listed by residue class e mod 8, are cut into
+//    8 contiguous runs, one per XCD (workgroup b runs on XCD b mod 8): for
+//    FC2 the classes themselves, for FC1 runs of equal weight (a unit's time
+//    is set by its weight stream, nearly whatever its rows, so every unit of
+//    a segment of up to 320 rows weighs 1; longer segments: their number of
+//    320-row chunks).  The 32 workgroups of an XCD walk its run in order and
+//    move through K at the same pace, so a token slice comes from HBM once
+//    per XCD that holds units of its expert and is then served by that XCD's
+//    L2.
 //  * 256-row pass: the four wavefronts form a 2x2 grid of 128 weight rows x
 //    up to 128 tokens each (256 accumulation registers).  Weight slices (HBM)
 //    are loaded with plain 16-byte loads into registers two 64-wide K stages
@@ -64,7 +69,7 @@ constexpr int W_SLOT = WROWS * CPR;    // 16-byte chunks of a weight stage
 constexpr int X_SLOT = XROWS_B * CPR;  // 16-byte chunks of a token stage
 constexpr int kNxcd = 8;
 constexpr int BIG_BLOCKS = 6;           // 32-row weight blocks of a unit for 257..320-row segments
-static_assert((2 * W_SLOT + 2 * X_SLOT) * 16 + 12 * kMaxE + 64 <= 160 * 1024, "LDS budget");
+static_assert((2 * W_SLOT + 2 * X_SLOT) * 16 + 14 * kMaxE + 64 <= 160 * 1024, "LDS budget");
 
 // Physical 16-byte slot of logical chunk `ch` of row `row` in a stage (8
 // chunks per row, 2 rows per 256-byte LDS line): the XOR spreads the 16 rows
@@ -693,10 +698,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int n_big = MODE == 0 ? (Nout / 16 + BIG_BLOCKS - 1) / BIG_BLOCKS : (Nout / 32 + BIG_BLOCKS - 1) / BIG_BLOCKS;
     __shared__ u32x4 wlds[2 * W_SLOT];
     __shared__ u32x4 xlds[2 * X_SLOT];
-    __shared__ int s_list[kMaxE];      // active experts of this XCD, ascending
+    __shared__ short s_list[kMaxE];    // active experts, by residue class mod nxcd, then ascending
     __shared__ int s_rows[kMaxE];      // their row counts (clipped to R)
-    __shared__ int s_pref[kMaxE + 1];  // first work item of each of them
+    __shared__ int s_pref[kMaxE + 1];  // first unit of each of them
+    __shared__ int s_wpref[kMaxE + 1]; // weighted position of that unit
     __shared__ int s_cnt;
+    __shared__ int s_cstart[kNxcd + 1];   // first unit of each residue class
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -705,11 +712,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int nxcd = (G % kNxcd == 0) ? kNxcd : 1;
     const int xcd = b % nxcd, P = G / nxcd, j = b / nxcd;
 
-    // ---- this XCD's experts that have rows (wavefront 0, ballot compaction) --
+    // ---- every expert with rows, its units and their weight (wavefront 0:
+    // ballot compaction and wavefront prefix sums), listed by residue class
+    // e mod nxcd.  A unit weighs the number of token chunks it takes (1 up to
+    // 320 rows): units stream the same weight bytes, so their time depends
+    // little on the rows below that. ----
     if (wave == 0) {
-        int run = 0;
-        for (int c = 0; c * nxcd < E; c += 64) {
-            const int e = xcd + nxcd * (c + lane);
+        int run = 0, run_u = 0, run_w = 0;
+        const int nc = (E + 64 * nxcd - 1) / (64 * nxcd) * 64;         // list positions per residue class
+        for (int c = 0; c < nxcd * nc; c += 64) {
+            const int e = c / nc + nxcd * (c % nc + lane);
+            if (c % nc == 0 && lane == 0) s_cstart[c / nc] = run_u;
             int m = 0;
             if (e < E) {
                 const long long so = seg_off[e];
@@ -717,30 +730,59 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 if (so + mm > R) mm = R - so;
                 m = (int)mm;
             }
+            // segments of 257..320 rows take BIG_BLOCKS-block units (one pass)
+            const int nu = m == 0 ? 0 : (!OUTQ && m > XROWS_A && m <= XROWS_B) ? n_big : n_units;
+            const int wu = m > XROWS_B ? min((m + XROWS_B - 1) / XROWS_B, 1024) : 1;
+            int iu = nu, iw = nu * wu;           // inclusive prefix sums over the lanes
+            for (int d = 1; d < 64; d <<= 1) {
+                const int su = __shfl_up(iu, d), sw = __shfl_up(iw, d);
+                if (lane >= d) { iu += su; iw += sw; }
+            }
             const unsigned long long act = __ballot(m > 0);
             if (m > 0) {
                 const int pos = run + __popcll(act & ((1ull << lane) - 1ull));
-                s_list[pos] = e;
+                s_list[pos] = (short)e;
                 s_rows[pos] = m;
+                s_pref[pos] = run_u + iu - nu;
+                s_wpref[pos] = run_w + iw - nu * wu;
             }
             run += __popcll(act);
+            run_u += __shfl(iu, 63);
+            run_w += __shfl(iw, 63);
         }
         if (lane == 0) {
-            // segments of 257..320 rows take BIG_BLOCKS-block units (one pass)
-            int acc_u = 0;
-            for (int i = 0; i < run; ++i) {
-                s_pref[i] = acc_u;
-                acc_u += (!OUTQ && s_rows[i] > XROWS_A && s_rows[i] <= XROWS_B) ? n_big : n_units;
-            }
-            s_pref[run] = acc_u;
+            s_cstart[nxcd] = run_u;
+            s_pref[run] = run_u;
+            s_wpref[run] = run_w;
             s_cnt = run;
         }
     }
     __syncthreads();
-    const int total = s_pref[s_cnt];
+    // XCD x takes one contiguous run of the list's units and its workgroups
+    // walk it in order, so an expert's token slices are read from HBM once
+    // per XCD that holds units of it.  FC1: the units whose weighted start
+    // lies in [x W / n, (x+1) W / n), equal runs that move at most a few
+    // experts' units across class boundaries.  FC2: residue class x exactly
+    // (measured faster than equal runs: its units then take longer).  The
+    // classes differ by a few units; FC1's units are long enough for that to
+    // add a unit to some workgroups' share.
+    const int cnt = s_cnt, wtot = s_wpref[cnt];
+    auto unit_at = [&](int pos) {              // first unit whose weighted start is >= pos
+        if (pos >= wtot) return s_pref[cnt];
+        int lo = 0, hi = cnt - 1;              // last slot whose start is <= pos
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_wpref[mid] <= pos) lo = mid; else hi = mid - 1;
+        }
+        const int nu = s_pref[lo + 1] - s_pref[lo];
+        const int wu = (s_wpref[lo + 1] - s_wpref[lo]) / nu;
+        return s_pref[lo] + (pos - s_wpref[lo] + wu - 1) / wu;
+    };
+    const int t_lo = MODE == 0 ? unit_at((int)((long long)wtot * xcd / nxcd)) : s_cstart[xcd];
+    const int t_hi = MODE == 0 ? unit_at((int)((long long)wtot * (xcd + 1) / nxcd)) : s_cstart[xcd + 1];
 
-    for (int t = j; t < total; t += P) {
-        int lo = 0, hi = s_cnt - 1;          // last slot whose first item is <= t
+    for (int t = t_lo + j; t < t_hi; t += P) {
+        int lo = 0, hi = cnt - 1;            // last slot whose first unit is <= t
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_pref[mid] <= t) lo = mid; else hi = mid - 1;
