@@ -22,11 +22,10 @@
 //    FC2 into the fp8 format, cut them into chunks of 320 rows taken by two
 //    128-row passes (the token chunk is then read twice, from L2).
 //  * The units of all experts, listed by residue class e mod 8, are cut into
-//    8 contiguous runs, one per XCD (workgroup b runs on XCD b mod 8): for
-//    FC2 the classes themselves, for FC1 runs of equal weight (a unit's time
-//    is set by its weight stream, nearly whatever its rows, so every unit of
-//    a segment of up to 320 rows weighs 1; longer segments: their number of
-//    320-row chunks).  The 32 workgroups of an XCD walk its run in order and
+//    8 contiguous runs of equal weight, one per XCD (workgroup b runs on XCD
+//    b mod 8).  A unit's time is set by its weight stream, nearly whatever its
+//    rows, so every unit of a segment of up to 320 rows weighs 1 (longer
+//    segments: their number of 320-row chunks).  The 32 workgroups of an XCD walk its run in order and
 //    move through K at the same pace, so a token slice comes from HBM once
 //    per XCD that holds units of its expert and is then served by that XCD's
 //    L2.
@@ -706,7 +705,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __shared__ int s_pref[kMaxE + 1];  // first unit of each of them
     __shared__ int s_wpref[kMaxE + 1]; // weighted position of that unit
     __shared__ int s_cnt;
-    __shared__ int s_cstart[kNxcd + 1];   // first unit of each residue class
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -725,7 +723,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int nc = (E + 64 * nxcd - 1) / (64 * nxcd) * 64;         // list positions per residue class
         for (int c = 0; c < nxcd * nc; c += 64) {
             const int e = c / nc + nxcd * (c % nc + lane);
-            if (c % nc == 0 && lane == 0) s_cstart[c / nc] = run_u;
             int m = 0;
             if (e < E) {
                 const long long so = seg_off[e];
@@ -754,21 +751,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             run_w += __shfl(iw, 63);
         }
         if (lane == 0) {
-            s_cstart[nxcd] = run_u;
             s_pref[run] = run_u;
             s_wpref[run] = run_w;
             s_cnt = run;
         }
     }
     __syncthreads();
-    // XCD x takes one contiguous run of the list's units and its workgroups
-    // walk it in order, so an expert's token slices are read from HBM once
-    // per XCD that holds units of it.  FC1: the units whose weighted start
-    // lies in [x W / n, (x+1) W / n), equal runs that move at most a few
-    // experts' units across class boundaries.  FC2: residue class x exactly
-    // (measured faster than equal runs: its units then take longer).  The
-    // classes differ by a few units; FC1's units are long enough for that to
-    // add a unit to some workgroups' share.
+    // XCD x takes the units whose weighted start lies in [x W / n, (x+1) W / n):
+    // one contiguous run of the list, mostly residue class x, with at most a
+    // few experts' units moved across class boundaries.  Its workgroups walk
+    // the run in order, so an expert's token slices are read from HBM once
+    // per XCD that holds units of it.
     const int cnt = s_cnt, wtot = s_wpref[cnt];
     auto unit_at = [&](int pos) {              // first unit whose weighted start is >= pos
         if (pos >= wtot) return s_pref[cnt];
@@ -781,8 +774,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int wu = (s_wpref[lo + 1] - s_wpref[lo]) / nu;
         return s_pref[lo] + (pos - s_wpref[lo] + wu - 1) / wu;
     };
-    const int t_lo = MODE == 0 ? unit_at((int)((long long)wtot * xcd / nxcd)) : s_cstart[xcd];
-    const int t_hi = MODE == 0 ? unit_at((int)((long long)wtot * (xcd + 1) / nxcd)) : s_cstart[xcd + 1];
+    const int t_lo = unit_at((int)((long long)wtot * xcd / nxcd));
+    const int t_hi = unit_at((int)((long long)wtot * (xcd + 1) / nxcd));
 
     for (int t = t_lo + j; t < t_hi; t += P) {
         int lo = 0, hi = cnt - 1;            // last slot whose first unit is <= t
