@@ -126,8 +126,13 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Two floats -> two bf16 (lo in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950 (the same rounding as f32_to_bf16 for every
+// finite value; a NaN stays a quiet NaN).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
 }
 
 // FC2 output in the fp8 combine format: e4m3 codes [rows, Nout] and one fp32
@@ -317,6 +322,63 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
 #pragma unroll
                 for (int r = 0; r < 16; ++r) v[j][r] = acc_read(acc[j][i][r]);
             store_q128(v, tok < mv, lane, qo, (size_t)tok, Nout, ocol0);
+        } else if constexpr (i < NTB && NWB == 4 && (MODE == 0 || MODE == 1)) {
+            // Whole-line stores: the wavefront's outputs for this token block
+            // (FC1: 64 features = 128 B per token, FC2: 128 columns = 256 B)
+            // go through its own part of token slot 1, then leave as whole row
+            // segments, 16 bytes per lane.  Token slot 1 is free after the K
+            // loop (its last reads end at the final barrier) and is written
+            // next only after the following unit's prologue barrier.  Only
+            // this wavefront touches its part, and its LDS operations run in
+            // order, so no barrier is needed here.  Rows are padded by 16 bytes
+            // (consecutive rows start 4 banks apart), so every access is one
+            // base address plus a constant offset.
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int RB = MODE == 0 ? 128 : 256;              // bytes of a token row
+            constexpr int RS = RB + 16;                             // row stride in LDS
+            constexpr int NC = RB / 16;                             // 16-byte chunks per row
+            constexpr int RPI = 64 / NC;                            // token rows per store instruction
+            static_assert(4 * 32 * RS <= X_SLOT * 16, "epilogue staging fits token slot 1");
+            int ln;                                                 // the lane, kept from being hoisted
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+            char* st = (char*)(xlds + X_SLOT) + wave * (32 * RS);
+            char* wr = st + (ln & 31) * RS + (ln >> 5) * 8;        // this lane's token row, its 8-byte half
+            if constexpr (MODE == 0) {
+#pragma unroll
+                for (int j = 0; j < NWB / 2; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        float a[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float g = acc_read(acc[j][i][g4 * 4 + r]);
+                            const float u = acc_read(acc[j + NWB / 2][i][g4 * 4 + r]);
+                            a[r] = g / (1.f + __expf(-g)) * u;
+                        }
+                        uint2 v;
+                        v.x = pack_bf16x2(a[0], a[1]);
+                        v.y = pack_bf16x2(a[2], a[3]);
+                        *(uint2*)(wr + (j * 4 + g4) * 16) = v;
+                    }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NWB; ++j)
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        uint2 v;
+                        v.x = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 0]), acc_read(acc[j][i][g4 * 4 + 1]));
+                        v.y = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 2]), acc_read(acc[j][i][g4 * 4 + 3]));
+                        *(uint2*)(wr + (j * 4 + g4) * 16) = v;
+                    }
+            }
+            const int tok0 = (q + 2 * i) * 32, rl = ln / NC, ch = ln % NC;
+            const char* rd = st + rl * RS + ch * 16;
+            uint16_t* od = obase + (size_t)(tok0 + rl) * Nout + ocol0 + ch * 8;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const u32x4 v = *(const u32x4*)(rd + k * RPI * RS);
+                if (tok0 + k * RPI + rl < mv) *(u32x4*)(od + (size_t)(k * RPI) * Nout) = v;
+            }
         } else if constexpr (i < NTB) {
             __builtin_amdgcn_sched_barrier(0);
             const int tok = (q + 2 * i) * 32 + (lane & 31);
@@ -596,6 +658,9 @@ template <int MODE, bool OUTQ>
 __device__ __forceinline__ void half_pass(u32x4* xring, u32x4* wring, const uint16_t* X, const uint16_t* Wb,
                                           uint16_t* Out, QOut qo, long long seg, int me, int Kdim, int Nout, int n0,
                                           int wave, int lane) {
+    // the rings span both 256-row weight slots: every wavefront has finished
+    // the previous unit's whole-line epilogue (weight slot 1) before any DMA
+    lds_barrier();
     // weight DMA q of wavefront w fills slots (q*4+w)*64.. of a stage:
         // rows 8*(q*4+w)..+7, each lane the logical chunk of its slot
         int wofs[W_LD];
