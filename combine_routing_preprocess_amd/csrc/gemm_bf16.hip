@@ -379,6 +379,62 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
                 const u32x4 v = *(const u32x4*)(rd + k * RPI * RS);
                 if (tok0 + k * RPI + rl < mv) *(u32x4*)(od + (size_t)(k * RPI) * Nout) = v;
             }
+        } else if constexpr (i < NTB && NWB == 3 && !OUTQ) {
+            // The same whole-line path for the three-block pass (segments of
+            // 257..320 rows): FC2 96 columns = 192 B per token, FC1's
+            // interleaved blocks 48 features = 96 B; a unit's last blocks may
+            // not exist (vb), so the row width is counted at run time.
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int BB = MODE == 2 ? 32 : 64;                 // bytes per weight block and token
+            constexpr int RS = NWB * BB + 16;                       // padded row stride in LDS
+            constexpr int LPR = MODE == 2 ? 8 : 16;                 // lanes per row when storing
+            constexpr int RPI = 64 / LPR;                           // token rows per store instruction
+            static_assert(4 * 32 * RS <= X_SLOT * 16, "epilogue staging fits token slot 1");
+            const int nvb = min(NWB, max(0, vb - p * NWB));         // this wavefront's blocks that exist (uniform)
+            int ln;                                                 // the lane, kept from being hoisted
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+            char* st = (char*)(xlds + X_SLOT) + wave * (32 * RS);
+            char* wr = st + (ln & 31) * RS + (ln >> 5) * 8;
+#pragma unroll
+            for (int j = 0; j < NWB; ++j) {
+                if (j >= nvb) continue;
+                if constexpr (MODE == 2) {
+                    // rows 0..15 of the block gate, 16..31 up: accumulators r and r + 8
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        float a[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float gt = acc_read(acc[j][i][4 * g + r]);
+                            const float u = acc_read(acc[j][i][8 + 4 * g + r]);
+                            a[r] = gt / (1.f + __expf(-gt)) * u;
+                        }
+                        uint2 v;
+                        v.x = pack_bf16x2(a[0], a[1]);
+                        v.y = pack_bf16x2(a[2], a[3]);
+                        *(uint2*)(wr + j * BB + g * 16) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        uint2 v;
+                        v.x = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 0]), acc_read(acc[j][i][g4 * 4 + 1]));
+                        v.y = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 2]), acc_read(acc[j][i][g4 * 4 + 3]));
+                        *(uint2*)(wr + j * BB + g4 * 16) = v;
+                    }
+                }
+            }
+            const int tok0 = (q + 2 * i) * 32, rl = ln / LPR, ch = ln % LPR;
+            const bool cv = ch < nvb * (BB / 16);                   // this lane's 16 bytes exist
+            const char* rd = st + rl * RS + ch * 16;
+            uint16_t* od = obase + (size_t)(tok0 + rl) * Nout + ocol0 + ch * 8;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                if (cv && tok0 + k * RPI + rl < mv) {
+                    const u32x4 v = *(const u32x4*)(rd + k * RPI * RS);
+                    *(u32x4*)(od + (size_t)(k * RPI) * Nout) = v;
+                }
+            }
         } else if constexpr (i < NTB) {
             __builtin_amdgcn_sched_barrier(0);
             const int tok = (q + 2 * i) * 32 + (lane & 31);
