@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void k_combine(const u32x4* __restrict__ Y, in
                 u32x4 o;
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    o[w] = f32_to_bf16(acc[u][2 * w]) | (f32_to_bf16(acc[u][2 * w + 1]) << 16);
+                    o[w] = bf16x2_rne(acc[u][2 * w], acc[u][2 * w + 1]);
                 y[(size_t)t * nch + c] = o;
             }
         }
@@ -180,8 +180,8 @@ __global__ __launch_bounds__(256) void k_combine_fp8(const u32x4* __restrict__ Y
                 u32x4 o0, o1;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    o0[w] = f32_to_bf16(acc[u][2 * w]) | (f32_to_bf16(acc[u][2 * w + 1]) << 16);
-                    o1[w] = f32_to_bf16(acc[u][8 + 2 * w]) | (f32_to_bf16(acc[u][8 + 2 * w + 1]) << 16);
+                    o0[w] = bf16x2_rne(acc[u][2 * w], acc[u][2 * w + 1]);
+                    o1[w] = bf16x2_rne(acc[u][8 + 2 * w], acc[u][8 + 2 * w + 1]);
                 }
                 y[((size_t)t * nch + c) * 2] = o0;
                 y[((size_t)t * nch + c) * 2 + 1] = o1;

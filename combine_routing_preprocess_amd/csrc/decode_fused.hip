@@ -302,8 +302,8 @@ __device__ void reduce_expert(const FusedArgs& a, const float* __restrict__ w2s,
                 }
             }
             u32x2 o;
-            o[0] = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-            o[1] = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+            o[0] = bf16x2_rne(acc[0], acc[1]);
+            o[1] = bf16x2_rne(acc[2], acc[3]);
             *(u32x2*)(a.eo + (size_t)(seg + i0 + i) * a.H + h) = o;
         }
     }

@@ -225,11 +225,11 @@ __device__ __forceinline__ void fp8_pass(const uint8_t* __restrict__ Xq, const f
             *(float4*)((float*)Outv + orow) = o;
         } else {
             uint2 o;
-            o.x = f32_to_bf16(acc_g[t][0]) | (f32_to_bf16(acc_g[t][1]) << 16);
-            o.y = f32_to_bf16(acc_g[t][2]) | (f32_to_bf16(acc_g[t][3]) << 16);
+            o.x = bf16x2_rne(acc_g[t][0], acc_g[t][1]);
+            o.y = bf16x2_rne(acc_g[t][2], acc_g[t][3]);
             *(uint2*)((uint16_t*)Outv + orow) = o;
-            o.x = f32_to_bf16(acc_u[t][0]) | (f32_to_bf16(acc_u[t][1]) << 16);
-            o.y = f32_to_bf16(acc_u[t][2]) | (f32_to_bf16(acc_u[t][3]) << 16);
+            o.x = bf16x2_rne(acc_u[t][0], acc_u[t][1]);
+            o.y = bf16x2_rne(acc_u[t][2], acc_u[t][3]);
             *(uint2*)((uint16_t*)Outv + orow + 16) = o;
         }
     }
@@ -393,7 +393,7 @@ __device__ __forceinline__ void combine_token_wg(const u32x4* __restrict__ Y, in
                 u32x4 o;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    o[q] = f32_to_bf16(acc[u][2 * q]) | (f32_to_bf16(acc[u][2 * q + 1]) << 16);
+                    o[q] = bf16x2_rne(acc[u][2 * q], acc[u][2 * q + 1]);
                 y[(size_t)t * nch + c] = o;
             }
         }

@@ -23,6 +23,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return u >> 16;
 }
+// Two floats -> two bf16 bits (lo in the low half) by gfx950's packed
+// conversion (v_cvt_pk_bf16_f32): round to nearest even, the same result as
+// f32_to_bf16 for every finite value.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
