@@ -432,63 +432,7 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
                 }
             }
         } else if constexpr (i < NTB) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int tok = (q + 2 * i) * 32 + (lane & 31);
-            if (tok < mv) {
-                uint16_t* orow = obase + (size_t)tok * Nout + ocol0 + (lane >> 5) * 4;
-                if (MODE == 2) {
-                    // interleaved blocks: rows 0..15 gate, 16..31 up of 16 features;
-                    // accumulator r (gate) and r + 8 (up) hold the same feature
-#pragma unroll
-                    for (int j = 0; j < NWB; ++j) {
-                        if (p * NWB + j >= vb) continue;
-#pragma unroll
-                        for (int g = 0; g < 2; ++g) {
-                            float a[4];
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float gt = acc_read(acc[j][i][4 * g + r]);
-                                const float u = acc_read(acc[j][i][8 + 4 * g + r]);
-                                a[r] = gt / (1.f + __expf(-gt)) * u;
-                            }
-                            uint2 v;
-                            v.x = pack_bf16x2(a[0], a[1]);
-                            v.y = pack_bf16x2(a[2], a[3]);
-                            *(uint2*)(orow + j * 16 + g * 8) = v;
-                        }
-                    }
-                } else if (MODE == 0) {
-                    // gate blocks 0..NWB/2-1, up blocks NWB/2..NWB-1 (same features)
-#pragma unroll
-                    for (int j = 0; j < NWB / 2; ++j)
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            float a[4];
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const float g = acc_read(acc[j][i][g4 * 4 + r]);
-                                const float u = acc_read(acc[j + NWB / 2][i][g4 * 4 + r]);
-                                a[r] = g / (1.f + __expf(-g)) * u;
-                            }
-                            uint2 v;
-                            v.x = pack_bf16x2(a[0], a[1]);
-                            v.y = pack_bf16x2(a[2], a[3]);
-                            *(uint2*)(orow + j * 32 + g4 * 8) = v;
-                        }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < NWB; ++j) {
-                        if (p * NWB + j >= vb) continue;
-#pragma unroll
-                        for (int g4 = 0; g4 < 4; ++g4) {
-                            uint2 v;
-                            v.x = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 0]), acc_read(acc[j][i][g4 * 4 + 1]));
-                            v.y = pack_bf16x2(acc_read(acc[j][i][g4 * 4 + 2]), acc_read(acc[j][i][g4 * 4 + 3]));
-                            *(uint2*)(orow + j * 32 + g4 * 8) = v;
-                        }
-                    }
-                }
-            }
+            static_assert(NWB == 0, "every pass shape has a staged epilogue above");
         }
     };
     store_block(std::integral_constant<int, 0>{});
