@@ -486,6 +486,17 @@ __device__ __forceinline__ void run_pass(u32x4* wlds, u32x4* xlds, const char* W
     const uint32_t xoff_last = (uint32_t)min(xr, mv - 1 - (NXB - 1) * 32) * (uint32_t)pitch + (uint32_t)xch * 16u;
     const int nk = Kdim / BK;
     const int ocol0 = MODE != 1 ? f0 + p * 16 * NWB : f0 + p * 32 * NWB;
+    // a unit's last blocks may not exist (vb): wavefronts with none of its
+    // blocks only load and keep the barriers, with no MFMAs (the three-block
+    // pass, whose experts' last unit holds 2 of 6 blocks)
+    if constexpr (NWB == 3) {
+        if (p * NWB >= vb) {
+            pass<MODE, OUTQ, NWB, NXB, 0>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff, xoff_last,
+                                          pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p, q, mv, ochunk,
+                                          Nout, ocol0, qo, vb);
+            return;
+        }
+    }
     if (q == 0)
         pass<MODE, OUTQ, NWB, NXB, (NXB + 1) / 2>(wlds, xlds, uniform_ptr(We), wrow, uniform_ptr(Xc), voff, xoff,
                                                   xoff_last, pitch, nk, lane, __builtin_amdgcn_readfirstlane(wave), p,
