@@ -375,7 +375,7 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
                 const u32x4 v = *(const u32x4*)(rd + k * RPI * RS);
                 if (tok0 + k * RPI + rl < mv) *(u32x4*)(od + (size_t)(k * RPI) * Nout) = v;
             }
-        } else if constexpr (i < NTB && NWB == 3 && !OUTQ) {
+        } else if constexpr (i < NTB && NWB <= 3 && !OUTQ) {
             // The same whole-line path for the three-block pass (segments of
             // 257..320 rows): FC2 96 columns = 192 B per token, FC1's
             // interleaved blocks 48 features = 96 B; a unit's last blocks may
@@ -867,10 +867,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int f0 = nt * BIG_BLOCKS * bsz;
             const int vb = min(BIG_BLOCKS, Nout / bsz - nt * BIG_BLOCKS);
             const QOut qn = {nullptr, nullptr};
-            if ((me + 31) / 32 == 9)
+            // a unit of at most 2 blocks (an expert's last) takes one block per wavefront pair
+            if (vb <= 2) {
+                if ((me + 31) / 32 == 9)
+                    run_pass<MODE == 0 ? 2 : 1, false, 1, 9>(wlds, xlds, We, Xc, Kdim, Nout, f0, me, oc, qn, lane, p, q, vb);
+                else
+                    run_pass<MODE == 0 ? 2 : 1, false, 1, 10>(wlds, xlds, We, Xc, Kdim, Nout, f0, me, oc, qn, lane, p, q, vb);
+            } else if ((me + 31) / 32 == 9) {
                 run_pass<MODE == 0 ? 2 : 1, false, 3, 9>(wlds, xlds, We, Xc, Kdim, Nout, f0, me, oc, qn, lane, p, q, vb);
-            else
+            } else {
                 run_pass<MODE == 0 ? 2 : 1, false, 3, 10>(wlds, xlds, We, Xc, Kdim, Nout, f0, me, oc, qn, lane, p, q, vb);
+            }
             continue;
         }
         const long long seg = seg_off[e];
