@@ -867,8 +867,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             const int f0 = nt * BIG_BLOCKS * bsz;
             const int vb = min(BIG_BLOCKS, Nout / bsz - nt * BIG_BLOCKS);
             const QOut qn = {nullptr, nullptr};
-            // a unit of at most 2 blocks (an expert's last) takes one block per wavefront pair
-            if (vb <= 2) {
+            // FC2: a unit of at most 2 blocks (an expert's last) takes one block
+            // per wavefront pair.  (FC1 keeps the three-block pass: there the
+            // faster unit ran ahead of its expert's others and re-read their
+            // token slice from HBM, for no gain in time.)
+            if (MODE == 1 && vb <= 2) {
                 if ((me + 31) / 32 == 9)
                     run_pass<MODE == 0 ? 2 : 1, false, 1, 9>(wlds, xlds, We, Xc, Kdim, Nout, f0, me, oc, qn, lane, p, q, vb);
                 else
