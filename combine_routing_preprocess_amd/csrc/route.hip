@@ -385,6 +385,8 @@ __global__ __launch_bounds__(1024) void k_route_small(const void* __restrict__ r
     const bool mine = wv < n_tiles && t < T;
     int err = 0;
     constexpr int U = 8;                   // slots loaded together, so their latencies overlap
+    int keep_e[U];                         // K <= U: the slots stay in registers for step 3
+    float keep_p[U];
     if (mine) {
         const bool live = t < T_live;
         const unsigned long long bit = 1ull << lane;
@@ -420,8 +422,13 @@ __global__ __launch_bounds__(1024) void k_route_small(const void* __restrict__ r
                         }
                     }
                 }
-                row_id[at] = oute;
-                copy_prob[at] = p;
+                if (K <= U) {
+                    keep_e[u] = oute;
+                    keep_p[u] = p;
+                } else {
+                    row_id[at] = oute;
+                    copy_prob[at] = p;
+                }
             }
         }
     }
@@ -469,7 +476,8 @@ __global__ __launch_bounds__(1024) void k_route_small(const void* __restrict__ r
     }
     __syncthreads();
 
-    // 3. final rows of tile wv's slots (each thread re-reads only its own slots)
+    // 3. final rows of tile wv's slots (each thread takes only its own slots: from
+    // registers when K <= U, else re-read)
     if (mine) {
         const unsigned long long below = (1ull << lane) - 1ull;
         for (int j0 = 0; j0 < K; j0 += U) {
@@ -478,19 +486,26 @@ __global__ __launch_bounds__(1024) void k_route_small(const void* __restrict__ r
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const size_t at = (size_t)t * K + min(j0 + u, K - 1);
-                ev[u] = row_id[at];
-                pv[u] = copy_prob[at];
+                ev[u] = K <= U ? keep_e[u] : row_id[at];
+                pv[u] = K <= U ? keep_p[u] : copy_prob[at];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (j0 + u >= K) break;
                 const int e = ev[u];
-                if (e < 0) continue;
                 const size_t at = (size_t)t * K + j0 + u;
+                if (e < 0) {
+                    if (K <= U) {              // step 1 left this slot in registers
+                        row_id[at] = -1;
+                        copy_prob[at] = 0.f;
+                    }
+                    continue;
+                }
                 const int rank = tbase[wv][e] + __popcll(msk[wv][e] & below);
                 const long long row = s_off[e] + rank;
                 if (rank < s_kept[e] && row < R) {
                     row_id[at] = (int)row;
+                    if (K <= U) copy_prob[at] = pv[u];    // step 1 left this slot in registers
                     src_row[row] = t;
                     if (out_probs) out_probs[row] = pv[u];
                 } else {
@@ -500,21 +515,18 @@ __global__ __launch_bounds__(1024) void k_route_small(const void* __restrict__ r
             }
         }
     }
-    // 4. rows that hold no copy: padding inside segments, everything past the last one
-    for (long long r = tid; r < R; r += 1024) {
-        bool assigned = false;
-        if (r < s_off[E]) {
-            int lo = 0, hi = E - 1;              // last e with s_off[e] <= r
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_off[mid] <= r) lo = mid; else hi = mid - 1;
-            }
-            assigned = r < s_off[lo] + s_kept[lo];
-        }
-        if (!assigned) {
+    // 4. rows that hold no copy: each expert's padding (by the thread of that
+    // expert), then everything past the last segment
+    if (tid < E) {
+        const long long end = min(s_off[tid + 1], R);
+        for (long long r = s_off[tid] + s_kept[tid]; r < end; ++r) {
             src_row[r] = -1;
             if (out_probs) out_probs[r] = 0.f;
         }
+    }
+    for (long long r = s_off[E] + tid; r < R; r += 1024) {
+        src_row[r] = -1;
+        if (out_probs) out_probs[r] = 0.f;
     }
     if (tid == 0) *flag = sflag;
 }
