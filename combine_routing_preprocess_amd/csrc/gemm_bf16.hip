@@ -241,7 +241,7 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
                 acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf][j], xf[buf][i], acc[j][i], 0, 0, 0);
     };
     constexpr int NMF = NWB * (NTB > 0 ? NTB : 1);      // MFMAs per step
-    constexpr bool DMA_FIRST = NXB > 8;
+    constexpr bool DMA_FIRST = NXB > 8 || MODE == 0;
     auto gload_h = [&](u32x4 (&sw)[NWL], int kt, int hh) {   // half hh of the refill loads
         const int k = min(kt, nk - 1) * (BK * 2);
 #pragma unroll
@@ -266,10 +266,10 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
             if (NTB > 0 && st + 1 < KS) frags(slot, st + 1, (st + 1) & 1);
             if (NTB > 0) mfmas(st & 1);
             // step 0 copies weight stage kt+1 into LDS, step 1 issues the token
-            // DMA of stage kt+1.  A pass of more than 8 token blocks issues its
-            // larger DMA in step 0 too, right after the copy (whose wait for the
-            // weight registers, placed by the compiler, does not see the DMA),
-            // so that it lands before the stage's closing wait.
+            // DMA of stage kt+1.  FC1, and a pass of more than 8 token blocks,
+            // issue the DMA in step 0 too, right after the copy (whose wait for
+            // the weight registers, placed by the compiler, does not see the
+            // DMA), so that it lands before the stage's closing wait.
             if (st == 0) {
                 swrite(sw, slot ^ 1);
                 if (DMA_FIRST) xdma(kt_x, slot ^ 1);
