@@ -219,9 +219,13 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
     const uint32_t xl0 = lds_addr_of(xlds) + wave * 64 * 16;
     auto xdma = [&](int kt, int slot) {   // token stage kt -> LDS slot (NXB instructions per wavefront)
         const int k = min(kt, nk - 1) * (BK * 2);
+        // a stage past the end is never read: every lane takes the same 16
+        // bytes (one line per instruction, the count in flight unchanged)
+        const bool live = kt < nk;
+        const uint32_t xo = live ? xoff : 0u, xol = live ? xoff_last : 0u;
 #pragma unroll
         for (int b = 0; b < NXB; ++b)
-            dma16(xbase + ((size_t)(b * 32) * pitch + k), b == NXB - 1 ? xoff_last : xoff,
+            dma16(xbase + ((size_t)(b * 32) * pitch + k), b == NXB - 1 ? xol : xo,
                   xl0 + (slot * X_SLOT + b * 256) * 16);
     };
     bf16x8 wf[2][NWB], xf[2][NTB > 0 ? NTB : 1];
@@ -244,10 +248,11 @@ __device__ __forceinline__ void pass(u32x4* wlds, u32x4* xlds, gchar* wbase, con
     constexpr bool DMA_FIRST = NXB > 8 || MODE == 0;
     auto gload_h = [&](u32x4 (&sw)[NWL], int kt, int hh) {   // half hh of the refill loads
         const int k = min(kt, nk - 1) * (BK * 2);
+        const uint32_t vo = kt < nk ? voff : 0u;   // past the end: one line per load, as in xdma
 #pragma unroll
         for (int b = 0; b < NWL; ++b)
             if (b % 2 == hh)
-                sw[b] = __builtin_nontemporal_load((const gu32x4*)(wbase + ((size_t)wrow[b] * pitch + k) + voff));
+                sw[b] = __builtin_nontemporal_load((const gu32x4*)(wbase + ((size_t)wrow[b] * pitch + k) + vo));
     };
     // One stage: 4 K steps of LDS slot `slot`; step s issues the fragment
     // reads of step s+1 and one kind of side work, interleaved one by one with
